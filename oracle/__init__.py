@@ -1,0 +1,317 @@
+"""CPU oracle and comparator for D = alpha * op(A) * op(B) + beta * C.
+
+TEST INFRASTRUCTURE ONLY.  The GPU library (``mixed_precision_dense_amd``) never imports,
+links or calls anything in this package, and this package imports nothing from it.  Only
+``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` use it.
+
+The arithmetic lives in ``mpgemm_oracle.c`` (plain C, fp64 / int64); this module builds it
+with gcc, wraps it with ctypes, and holds the comparator that decides whether a GPU result
+is acceptable.  Every stored array is a numpy array of raw storage: FP16 and BF16 as
+``uint16`` bit patterns, FP32 as ``float32``, INT8 as ``int8``, INT32 as ``int32``, each
+row-major with an explicit leading dimension.
+
+Pages (cited by title and section):
+  * "Programming Tensor Cores in CUDA 9" (makelele.cn/d/1827294.html) -- the GEMM call and
+    its alpha/beta epilogue (sections on cuBLAS usage and "Finishing").
+  * "Mixed-Precision Programming with CUDA 8" (m.ruidan.com/infomation/detail/138780) --
+    number formats (Figure 1) and the DP4A integer dot product (Figure 2).
+  * "NVIDIA Tensor Core mixed-precision computing: principles and applications"
+    (jsqmd.com/news/1087138) -- section 2.3, rounding model and the error expression
+    E = sum(a_i b_i)(1 + d_i) + c(1 + d_c), |d| <= 2^-p, which the bound below instantiates
+    with FP32's p = 23.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mpgemm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmpgemm_oracle.so")
+
+# Type codes private to the oracle (mirrors the enum in mpgemm_oracle.c).
+_CODES = {"f16": 0, "bf16": 1, "i8": 2, "f32": 3, "i32": 4}
+_STORAGE = {"f16": np.uint16, "bf16": np.uint16, "i8": np.int8, "f32": np.float32,
+            "i32": np.int32}
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction) and return its path."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def _load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+        lib.oracle_decode.restype = dbl
+        lib.oracle_decode.argtypes = [ctypes.c_uint64, i32, i32]
+        lib.oracle_encode_rne.restype = ctypes.c_uint64
+        lib.oracle_encode_rne.argtypes = [dbl, i32, i32]
+        lib.oracle_gemm_fp_points.restype = i32
+        lib.oracle_gemm_fp_points.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i32, i64, vp,
+                                              i32, i64, dbl, vp, i32, i64, i64, vp, vp, vp,
+                                              vp, vp]
+        lib.oracle_gemm_fp_full.restype = i32
+        lib.oracle_gemm_fp_full.argtypes = [i32, i32, i64, i64, i64, dbl, vp, i32, i64, vp,
+                                            i32, i64, dbl, vp, i32, i64, vp, vp, vp]
+        lib.oracle_gemm_int_points.restype = i32
+        lib.oracle_gemm_int_points.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, vp, i64,
+                                               i64, vp, i64, i64, vp, vp, vp]
+        lib.oracle_gemm_int_full.restype = i32
+        lib.oracle_gemm_int_full.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, vp, i64,
+                                             i64, vp, i64, vp]
+        lib.oracle_round_array.restype = i32
+        lib.oracle_round_array.argtypes = [vp, i64, i32, vp]
+        lib.oracle_num_threads.restype = i32
+        lib.oracle_num_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return int(_load().oracle_num_threads())
+
+
+# ----------------------------------------------------------------------------- formats
+_FIELDS = {"f16": (5, 10), "bf16": (8, 7), "f32": (8, 23)}
+
+
+def decode(bits: int, fmt: str) -> float:
+    """Value of one bit pattern of ``fmt`` ('f16', 'bf16', 'f32'), from the field definition."""
+    e, m = _FIELDS[fmt]
+    return float(_load().oracle_decode(int(bits), e, m))
+
+
+def encode_rne(value: float, fmt: str) -> int:
+    """Bit pattern of ``value`` rounded to nearest-even in ``fmt``."""
+    e, m = _FIELDS[fmt]
+    return int(_load().oracle_encode_rne(float(value), e, m))
+
+
+def round_to(v: np.ndarray, fmt: str) -> np.ndarray:
+    """Round float64 values once (nearest-even) to ``fmt``; returns raw storage."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint32 if fmt == "f32" else np.uint16)
+    rc = _load().oracle_round_array(v.ctypes.data, v.size, _CODES[fmt], out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle cannot round to {fmt}")
+    return out.view(np.float32) if fmt == "f32" else out
+
+
+# ----------------------------------------------------------------------------- GEMM
+@dataclass
+class FpReference:
+    """Oracle result for floating-point outputs, per output element."""
+    v: np.ndarray    # alpha*s + beta*c in double, before output rounding
+    S: np.ndarray    # sum_p |a(i,p) * b(p,j)|
+    bc: np.ndarray   # beta * c (0 where beta == 0)
+
+
+def _ptr(a: Optional[np.ndarray]) -> Optional[int]:
+    return None if a is None else a.ctypes.data
+
+
+def _check_storage(name: str, arr: Optional[np.ndarray], fmt: str) -> None:
+    if arr is None:
+        return
+    if arr.dtype != _STORAGE[fmt]:
+        raise TypeError(f"{name}: expected storage {np.dtype(_STORAGE[fmt])} for {fmt}, "
+                        f"got {arr.dtype}")
+    if not arr.flags.c_contiguous:
+        raise ValueError(f"{name} must be C-contiguous raw storage")
+
+
+def gemm_fp(transa: bool, transb: bool, m: int, n: int, k: int, alpha: float,
+            A: np.ndarray, atype: str, lda: int, B: np.ndarray, btype: str, ldb: int,
+            beta: float, C: Optional[np.ndarray], ctype: str, ldc: int,
+            points: Optional[tuple] = None) -> FpReference:
+    """Floating-point oracle.  With ``points=(ii, jj)`` only those elements are computed
+    (each one from the definition); otherwise the full m x n output."""
+    _check_storage("A", A, atype)
+    _check_storage("B", B, btype)
+    if beta != 0.0:
+        _check_storage("C", C, ctype)
+    else:
+        C = None
+    lib = _load()
+    args = (int(bool(transa)), int(bool(transb)), m, n, k, float(alpha), _ptr(A),
+            _CODES[atype], lda, _ptr(B), _CODES[btype], ldb, float(beta), _ptr(C),
+            _CODES[ctype], ldc)
+    if points is None:
+        v = np.empty((m, n), np.float64)
+        S = np.empty((m, n), np.float64)
+        bc = np.empty((m, n), np.float64)
+        rc = lib.oracle_gemm_fp_full(*args, v.ctypes.data, S.ctypes.data, bc.ctypes.data)
+    else:
+        ii = np.ascontiguousarray(points[0], dtype=np.int64)
+        jj = np.ascontiguousarray(points[1], dtype=np.int64)
+        v = np.empty(ii.shape, np.float64)
+        S = np.empty(ii.shape, np.float64)
+        bc = np.empty(ii.shape, np.float64)
+        rc = lib.oracle_gemm_fp_points(*args, ii.size, ii.ctypes.data, jj.ctypes.data,
+                                       v.ctypes.data, S.ctypes.data, bc.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle rejected types a={atype} b={btype} c={ctype} (rc={rc})")
+    return FpReference(v, S, bc)
+
+
+def gemm_int(transa: bool, transb: bool, m: int, n: int, k: int, alpha: int,
+             A: np.ndarray, lda: int, B: np.ndarray, ldb: int, beta: int,
+             C: Optional[np.ndarray], ldc: int, points: Optional[tuple] = None) -> np.ndarray:
+    """INT8 x INT8 -> INT32 oracle (exact, wraps modulo 2^32).  Returns int32 values."""
+    _check_storage("A", A, "i8")
+    _check_storage("B", B, "i8")
+    if beta != 0:
+        _check_storage("C", C, "i32")
+    else:
+        C = None
+    lib = _load()
+    args = (int(bool(transa)), int(bool(transb)), m, n, k, int(alpha), _ptr(A), lda, _ptr(B),
+            ldb, int(beta), _ptr(C), ldc)
+    if points is None:
+        d = np.empty((m, n), np.int32)
+        lib.oracle_gemm_int_full(*args, d.ctypes.data)
+    else:
+        ii = np.ascontiguousarray(points[0], dtype=np.int64)
+        jj = np.ascontiguousarray(points[1], dtype=np.int64)
+        d = np.empty(ii.shape, np.int32)
+        lib.oracle_gemm_int_points(*args, ii.size, ii.ctypes.data, jj.ctypes.data,
+                                   d.ctypes.data)
+    return d
+
+
+# ----------------------------------------------------------------------------- comparator
+_OUT_ROUNDING = {
+    # unit roundoff of the output format and half its smallest subnormal spacing
+    "f16": (2.0 ** -11, 2.0 ** -25),
+    "bf16": (2.0 ** -8, 2.0 ** -134),
+}
+
+
+def output_to_f64(D: np.ndarray, fmt: str) -> np.ndarray:
+    """Widen raw output storage to float64 (exact conversions)."""
+    if fmt == "f32":
+        return np.asarray(D).view(np.float32).astype(np.float64)
+    if fmt == "f16":
+        return np.asarray(D).view(np.float16).astype(np.float64)
+    if fmt == "bf16":
+        return (np.asarray(D).view(np.uint16).astype(np.uint32) << 16).view(
+            np.float32).astype(np.float64)
+    raise ValueError(fmt)
+
+
+def _is_pow2_or_zero(x: float) -> bool:
+    if x == 0.0:
+        return True
+    mant, _ = np.frexp(abs(x))
+    return mant == 0.5
+
+
+@dataclass
+class CheckReport:
+    ok: bool
+    n: int
+    n_bad: int
+    worst_ratio: float          # max |D - v| / bound over finite elements (0 for exact mode)
+    first_bad: Optional[int]    # flat index of the first failing element
+    detail: str = ""
+
+    def __bool__(self) -> bool:
+        return self.ok
+
+
+def fp_bound(ref: FpReference, k: int, alpha: float, out_fmt: str,
+             underflow_floor: bool = False) -> np.ndarray:
+    """Per-element acceptance radius around the oracle's v.
+
+    FP32 accumulation (the Tensor Core numerics page, section 2.3, with p = 23):
+        E = |alpha| * K * 2^-23 * S + 2^-23 * |beta * c|
+    K becomes K + 1 when alpha is not 0 or a power of two (one more rounding in alpha*acc).
+    The oracle's own double summation error, (K-1) * 2^-53 * |alpha| * S, is added.
+    FP16/BF16 outputs add the final rounding: u * (|v| + E) + eta.
+    ``underflow_floor`` adds (K+1) * 2^-126 * max(|alpha|, 1) for directed subnormal-scale
+    cases, where flush-to-zero of FP32 intermediates is allowed.
+    """
+    keff = k if _is_pow2_or_zero(alpha) else k + 1
+    a = abs(alpha)
+    E = a * keff * 2.0 ** -23 * ref.S + 2.0 ** -23 * np.abs(ref.bc)
+    E = E + a * max(k - 1, 0) * 2.0 ** -53 * ref.S
+    if underflow_floor:
+        E = E + (k + 1) * 2.0 ** -126 * max(a, 1.0)
+    if out_fmt in _OUT_ROUNDING:
+        u, eta = _OUT_ROUNDING[out_fmt]
+        E = E + u * (np.abs(ref.v) + E) + eta
+    return E
+
+
+def check_fp(D: np.ndarray, out_fmt: str, ref: FpReference, k: int, alpha: float,
+             exact: bool = False, underflow_floor: bool = False) -> CheckReport:
+    """Accept or reject a floating-point GPU result against the oracle.
+
+    exact=True: bitwise equality with the oracle's once-rounded value (+0 == -0, any NaN ==
+    any NaN).  Otherwise: NaN where v is NaN, the same infinity where v is infinite, and
+    |D - v| <= bound elsewhere (an output that the oracle rounds to infinity may also be
+    that infinity)."""
+    Dv = output_to_f64(D, out_fmt).reshape(-1)
+    v = ref.v.reshape(-1)
+    n = v.size
+    ref_rounded = output_to_f64(round_to(v, out_fmt), out_fmt)
+    if exact:
+        same = (Dv == ref_rounded) | (np.isnan(Dv) & np.isnan(ref_rounded))
+        bad = ~same
+        worst = 0.0
+    else:
+        E = fp_bound(ref, k, alpha, out_fmt, underflow_floor).reshape(-1)
+        nan_v = np.isnan(v)
+        inf_v = np.isinf(v)
+        fin_v = ~(nan_v | inf_v)
+        bad = np.zeros(n, dtype=bool)
+        bad |= nan_v & ~np.isnan(Dv)
+        bad |= inf_v & ~(Dv == v)
+        with np.errstate(invalid="ignore", over="ignore"):
+            err = np.abs(Dv - v)
+            within = np.isfinite(Dv) & (err <= E)
+            overflow_ok = np.isinf(ref_rounded) & (Dv == ref_rounded)
+            bad |= fin_v & ~(within | overflow_ok)
+            ratio = np.where(fin_v & np.isfinite(Dv) & (E > 0), err / np.where(E > 0, E, 1),
+                             0.0)
+        worst = float(ratio.max()) if n else 0.0
+    idx = np.flatnonzero(bad)
+    first = int(idx[0]) if idx.size else None
+    detail = ""
+    if first is not None:
+        detail = (f"first bad flat index {first}: D={Dv[first]!r} v={v[first]!r} "
+                  f"ref_rounded={ref_rounded[first]!r}")
+    return CheckReport(ok=idx.size == 0, n=n, n_bad=int(idx.size), worst_ratio=worst,
+                       first_bad=first, detail=detail)
+
+
+def check_int(D: np.ndarray, ref: np.ndarray) -> CheckReport:
+    """INT32 outputs must equal the oracle bit for bit."""
+    d = np.asarray(D).view(np.int32).reshape(-1)
+    r = np.asarray(ref).view(np.int32).reshape(-1)
+    bad = d != r
+    idx = np.flatnonzero(bad)
+    first = int(idx[0]) if idx.size else None
+    detail = "" if first is None else f"first bad flat index {first}: D={d[first]} ref={r[first]}"
+    return CheckReport(ok=idx.size == 0, n=d.size, n_bad=int(idx.size), worst_ratio=0.0,
+                       first_bad=first, detail=detail)
