@@ -1,0 +1,215 @@
+"""Throughput of the mixed-precision GEMM on one MI355X.
+
+Default workload: FP16 4096 x 4096 x 4096, A row-major, B stored n x k (transb = T), beta = 0,
+FP32 accumulation and output -- one step is one D = alpha * A * B^T GEMM on inputs already
+resident in device memory.  Prints one JSON line with TFLOP/s, the roofline of the GEMM
+kernel (MFMA bound, measured with HIP events on the launch stream) and the CPU oracle's rate
+on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+  python bench.py --copy-calibration   # a plain copy of known size, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "mpgemm_f16_4096_nt_counters.txt")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "mixed_precision_dense_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    summary is missing, for another workload, or taken on different kernel sources."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("workload") != workload or kv.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
+    """A device-to-device copy of known size (for scaling FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def time_gemm(w, steps: int, warmup: int):
+    """Returns (wall ms per step, kernel ms per launch from HIP events, tile)."""
+    import torch
+    import mixed_precision_dense_amd as mp
+    from gemm_inputs import generate
+
+    inp = generate(w)
+    dA = mp.device_buffer(inp.A, w.in_type)
+    dB = mp.device_buffer(inp.B, w.in_type)
+    dC = mp.device_buffer(inp.C, w.out_type) if inp.C is not None else None
+    ob = {"f32": 4, "i32": 4, "f16": 2, "bf16": 2}[w.out_type]
+    dD = torch.empty(w.m * w.ldc * ob, dtype=torch.uint8, device="cuda")
+    compute = "i32" if w.in_type == "i8" else "f32"
+    alpha = int(w.alpha) if compute == "i32" else w.alpha
+    beta = int(w.beta) if compute == "i32" else w.beta
+    stream = torch.cuda.current_stream()
+    h = mp.Handle()
+
+    def step():
+        mp.mpgemm_run(h.h, w.transa, w.transb, w.m, w.n, w.k, alpha, dA, w.in_type, w.lda, dB,
+                      w.in_type, w.ldb, beta, dC, w.out_type, w.ldc, dD, compute, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # wall clock over exactly `steps` steps
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # kernel time: HIP events recorded on the stream the kernel is launched on
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    ev1.synchronize()
+    kern_ms = ev0.elapsed_time(ev1) / steps
+    tile = mp.mpgemm_tile_shape(w.m, w.n)
+    h.close()
+    return wall_ms, kern_ms, tile
+
+
+def cpu_baseline(w, target_s: float = 15.0):
+    """The oracle, as is, on a bounded sample of the workload's output elements."""
+    import numpy as np
+    import oracle
+    from gemm_inputs import generate, sample_points
+
+    inp = generate(w)
+    ref = oracle.gemm_int if w.in_type == "i8" else oracle.gemm_fp
+
+    def run(npts):
+        pts = sample_points(w.m, w.n, max(npts - 132, 1), seed=99)
+        t0 = time.perf_counter()
+        if w.in_type == "i8":
+            oracle.gemm_int(w.transa, w.transb, w.m, w.n, w.k, int(w.alpha), inp.A, w.lda, inp.B,
+                            w.ldb, int(w.beta), inp.C, w.ldc, points=pts)
+        else:
+            oracle.gemm_fp(w.transa, w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda,
+                           inp.B, w.in_type, w.ldb, w.beta, inp.C, w.out_type, w.ldc, points=pts)
+        return time.perf_counter() - t0, pts[0].size
+
+    t, npts = run(20000)                       # calibrate the sample size
+    want = int(npts * target_s / max(t, 1e-3))
+    want = max(20000, min(want, w.m * w.n))
+    t, npts = run(want)
+    tflops = 2.0 * npts * w.k / t / 1e12
+    return {"value": tflops, "unit": "TFLOP/s" if w.in_type != "i8" else "TOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{npts} output elements (random points plus the corners, last row and "
+                      f"last column) of the {w.m}x{w.n}x{w.k} workload, each a {w.k}-term "
+                      f"fp64 dot product plus |a*b| sum; {t:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="f16_4096_nt")
+    ap.add_argument("--all", action="store_true",
+                    help="also time every named workload (one line each on stderr)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the GEMM is measured on "
+              "a single MI355X; a multi-GPU run would shard D by output blocks and is not "
+              "built.", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    from gemm_inputs import WORKLOADS
+    w = WORKLOADS[args.workload]
+    wall_ms, kern_ms, tile = time_gemm(w, args.steps, args.warmup)
+    flops = w.flops
+    value = flops / (wall_ms * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.in_type]
+    unit = "TOP/s" if w.in_type == "i8" else "TFLOP/s"
+    traffic = recorded_traffic(w.name)
+    line = {
+        "metric": "TFLOP/s (TOP/s int8) and % of MI355X dense MFMA peak at 1 GPU",
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.in_type,
+        "data": "synthetic",
+        "config": {"workload": w.name, "m": w.m, "n": w.n, "k": w.k,
+                   "transa": "T" if w.transa else "N", "transb": "T" if w.transb else "N",
+                   "in": w.in_type, "accumulate": "i32" if w.in_type == "i8" else "f32",
+                   "out": w.out_type, "alpha": w.alpha, "beta": w.beta,
+                   "tile": f"{tile[0]}x{tile[1]}", "pct_of_peak": round(100 * value / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    if args.all:
+        for name, wx in WORKLOADS.items():
+            wm, km, tl = time_gemm(wx, max(10, args.steps // 2), args.warmup)
+            pk = PEAK_TFLOPS[wx.in_type]
+            rec = {"workload": name, "kernel_ms": round(km, 5), "wall_ms": round(wm, 5),
+                   "tflops_kernel": round(wx.flops / km / 1e9, 2),
+                   "pct_peak_kernel": round(100 * wx.flops / km / 1e9 / pk, 2),
+                   "tile": f"{tl[0]}x{tl[1]}"}
+            print(json.dumps(rec), file=sys.stderr, flush=True)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -117,6 +117,12 @@ def draw(rng: np.random.Generator, shape: tuple, dist: str, fmt: str) -> np.ndar
     return to_storage(x, fmt)
 
 
+def padded_ld(cols: int, fmt: str) -> int:
+    """Smallest leading dimension >= max(cols, 1) whose row size is a multiple of 16 bytes."""
+    per = 16 // ELEM_BYTES[fmt]
+    return ((max(cols, 1) + per - 1) // per) * per
+
+
 @dataclass
 class Workload:
     """A GEMM problem description plus the recipe of its synthetic inputs."""
@@ -140,11 +146,13 @@ class Workload:
     note: str = ""
 
     def __post_init__(self):
+        # default leading dimensions: the row length rounded up to a 16-byte multiple (and at
+        # least one element), the library's alignment contract
         ra, ca = stored_shape(self.m, self.k, self.transa)
         rb, cb = stored_shape(self.k, self.n, self.transb)
-        self.lda = ca if self.lda is None else self.lda
-        self.ldb = cb if self.ldb is None else self.ldb
-        self.ldc = self.n if self.ldc is None else self.ldc
+        self.lda = padded_ld(ca, self.in_type) if self.lda is None else self.lda
+        self.ldb = padded_ld(cb, self.in_type) if self.ldb is None else self.ldb
+        self.ldc = padded_ld(self.n, self.out_type) if self.ldc is None else self.ldc
 
     @property
     def flops(self) -> int:

@@ -1,0 +1,133 @@
+/*
+ * mpgemm.h -- mixed-precision dense matrix multiply-accumulate on AMD Instinct MI355X (gfx950).
+ *
+ *     D = alpha * op(A) * op(B) + beta * C
+ *
+ * with FP16 or BF16 inputs accumulated in FP32, or INT8 inputs accumulated in INT32.
+ *
+ * The call follows the GEMM statement of "Programming Tensor Cores in CUDA 9"
+ * (makelele.cn/d/1827294.html), section on using Tensor Cores through cuBLAS: a handle,
+ * transpose flags, m, n, k, alpha, the A, B and C matrices each with an element type and a
+ * leading dimension, beta, and a compute (accumulate) type; and its section "Finishing":
+ * the product is scaled by alpha and added to C scaled by beta.  The type matrix follows
+ * "Mixed-Precision Programming with CUDA 8" (m.ruidan.com/infomation/detail/138780),
+ * section on cuBLAS: FP32 compute on FP16 inputs with FP32 or FP16 output, and INT8 inputs
+ * with integer (DP4A-style) compute.
+ *
+ * STORAGE IS ROW-MAJOR.  op(A) is m x k, op(B) is k x n, C and D are m x n.
+ *   transa == MPGEMM_OP_N: A is stored m x k, element (i,p) at A[i*lda + p], lda >= k.
+ *   transa == MPGEMM_OP_T: A is stored k x m (the buffer holds op(A)^T), element (i,p) at
+ *                          A[p*lda + i], lda >= m.
+ *   transb == MPGEMM_OP_N: B is stored k x n, element (p,j) at B[p*ldb + j], ldb >= n.
+ *   transb == MPGEMM_OP_T: B is stored n x k ("B column-major"), element (p,j) at
+ *                          B[j*ldb + p], ldb >= k.
+ *   C and D: element (i,j) at [i*ldc + j], ldc >= n.  D has C's type and leading dimension.
+ * A column-major caller computes D^T = op(B)^T op(A)^T: it passes (transb, transa, n, m, k,
+ * B, ldb, A, lda, C, ldc), which the row-major reading turns back into its own problem.
+ *
+ * Supported type combinations (anything else returns MPGEMM_STATUS_NOT_SUPPORTED):
+ *   a_type = b_type = MPGEMM_R_16F,  compute MPGEMM_R_32F, c_type MPGEMM_R_32F or MPGEMM_R_16F
+ *   a_type = b_type = MPGEMM_R_16BF, compute MPGEMM_R_32F, c_type MPGEMM_R_32F or MPGEMM_R_16BF
+ *   a_type = b_type = MPGEMM_R_8I,   compute MPGEMM_R_32I, c_type MPGEMM_R_32I
+ * FP16/BF16 outputs are rounded once from the FP32 result, to nearest with ties to even.
+ * INT32 accumulation and the epilogue wrap modulo 2^32.
+ *
+ * Alignment contract (there is no slower fallback path): A, B, C (when read) and D must be
+ * 16-byte aligned, and lda, ldb, ldc times the element size must be multiples of 16 bytes
+ * (8 elements for FP16/BF16, 16 for INT8, 4 for FP32/INT32).  m, n and k are arbitrary.
+ * Operands are read in whole aligned 16-byte blocks: each row of A and B must be readable up
+ * to the end of the 16-byte block holding its last element (true of any buffer whose size is
+ * rows * ld elements).  Elements beyond the logical row are never used in the result.
+ * The distance in bytes spanned by 256 rows of any operand (256 * ld * element size) must be
+ * below 2^31; larger strides return MPGEMM_STATUS_NOT_SUPPORTED.
+ *
+ * Ownership and ordering: the caller allocates and owns every matrix and keeps it alive and
+ * unmodified until the work queued on `stream` has finished.  mpgemm_run allocates no device
+ * memory, is asynchronous, and is ordered on `stream` (a hipStream_t; NULL means the null
+ * stream).  A handle is bound to the device that was current at mpgemm_create and holds only
+ * host state; use one handle per host thread (a handle is not thread-safe).
+ *
+ * Errors are returned as status codes; nothing aborts and no exception crosses this ABI.
+ * Arguments are checked on the host before any device call.  Faults that happen while the
+ * queued kernel runs surface at the caller's next synchronisation of `stream`.
+ */
+#ifndef MPGEMM_H
+#define MPGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mpgemm_handle_s *mpgemm_handle_t;
+
+typedef enum { MPGEMM_OP_N = 0, MPGEMM_OP_T = 1 } mpgemm_op_t;
+
+typedef enum {
+    MPGEMM_R_16F = 0,   /* IEEE binary16: 1 sign, 5 exponent, 10 fraction bits */
+    MPGEMM_R_16BF = 1,  /* bfloat16: upper 16 bits of an IEEE binary32 */
+    MPGEMM_R_8I = 2,    /* signed 8-bit integer */
+    MPGEMM_R_32F = 3,   /* IEEE binary32 */
+    MPGEMM_R_32I = 4    /* signed 32-bit integer (two's complement) */
+} mpgemm_dtype_t;
+
+typedef enum {
+    MPGEMM_STATUS_SUCCESS = 0,
+    MPGEMM_STATUS_NOT_INITIALIZED = 1, /* handle not created, or already destroyed */
+    MPGEMM_STATUS_INVALID_VALUE = 2,   /* null pointer, negative size, ld below its minimum */
+    MPGEMM_STATUS_NOT_SUPPORTED = 3,   /* type combination, alignment or stride outside the contract */
+    MPGEMM_STATUS_ALLOC_FAILED = 4,    /* host allocation of the handle failed */
+    MPGEMM_STATUS_NO_DEVICE = 5,       /* no HIP device, or the current device is not gfx950 */
+    MPGEMM_STATUS_LAUNCH_FAILED = 6,   /* the kernel launch was rejected by the runtime */
+    MPGEMM_STATUS_INTERNAL_ERROR = 7,
+    MPGEMM_STATUS_WRONG_DEVICE = 8     /* current device differs from the handle's device */
+} mpgemm_status_t;
+
+/* Create a handle bound to the current HIP device.  Returns MPGEMM_STATUS_NO_DEVICE when no
+ * device is present or the device is not a gfx950, MPGEMM_STATUS_INVALID_VALUE when
+ * `handle` is NULL, MPGEMM_STATUS_ALLOC_FAILED when host memory runs out.  On failure
+ * *handle is set to NULL (when handle is non-NULL). */
+mpgemm_status_t mpgemm_create(mpgemm_handle_t *handle);
+
+/* Queue D = alpha * op(A) * op(B) + beta * C on `stream` (see the contract above).
+ *   alpha, beta: host pointers to a float (compute MPGEMM_R_32F) or an int32_t
+ *                (compute MPGEMM_R_32I), read before the call returns.
+ *   C:           read only when *beta != 0; may be NULL otherwise.  D == C (in place) is
+ *                allowed; any other overlap of D with A, B or C is undefined.
+ *   m == 0 or n == 0 returns MPGEMM_STATUS_SUCCESS without touching the device.
+ *   k == 0 gives D = beta * C (D = 0 when beta == 0); A and B may then be NULL.
+ *   alpha == 0 is not special-cased: NaN or Inf in A or B still reaches D.
+ * The current HIP device must be the handle's (else MPGEMM_STATUS_WRONG_DEVICE). */
+mpgemm_status_t mpgemm_run(mpgemm_handle_t handle, mpgemm_op_t transa, mpgemm_op_t transb,
+                           int64_t m, int64_t n, int64_t k, const void *alpha,
+                           const void *A, mpgemm_dtype_t a_type, int64_t lda,
+                           const void *B, mpgemm_dtype_t b_type, int64_t ldb,
+                           const void *beta, const void *C, mpgemm_dtype_t c_type, int64_t ldc,
+                           void *D, mpgemm_dtype_t compute_type, void *stream);
+
+/* Host-only argument check: returns exactly the status mpgemm_run would return for these
+ * arguments before touching the device (MPGEMM_STATUS_SUCCESS if it would launch).  It needs
+ * no handle and no device, and dereferences only alpha and beta. */
+mpgemm_status_t mpgemm_check(mpgemm_op_t transa, mpgemm_op_t transb, int64_t m, int64_t n,
+                             int64_t k, const void *alpha, const void *A, mpgemm_dtype_t a_type,
+                             int64_t lda, const void *B, mpgemm_dtype_t b_type, int64_t ldb,
+                             const void *beta, const void *C, mpgemm_dtype_t c_type, int64_t ldc,
+                             const void *D, mpgemm_dtype_t compute_type);
+
+/* Release a handle.  NULL or an unknown/destroyed handle returns
+ * MPGEMM_STATUS_NOT_INITIALIZED.  Work already queued is not affected. */
+mpgemm_status_t mpgemm_destroy(mpgemm_handle_t handle);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *mpgemm_status_string(mpgemm_status_t status);
+
+/* Tile shape (rows x columns of D per workgroup) that mpgemm_run picks for an m x n output,
+ * written to *tile_m and *tile_n.  Host-only; for diagnostics and benchmarks. */
+mpgemm_status_t mpgemm_tile_shape(int64_t m, int64_t n, int *tile_m, int *tile_n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MPGEMM_H */

@@ -1,0 +1,30 @@
+// Instances of the GEMM kernel for i8 inputs (one translation unit per input type so the
+// instances compile in parallel).
+#include "mpgemm_kernel.hpp"
+
+namespace mpg {
+
+template <int OUT, bool TA, bool TB>
+static hipError_t by_tile(int tile, const Params &p, hipStream_t s) {
+    switch (tile) {
+    case 256: return launch<IN_I8, OUT, TA, TB, 256, 256>(p, s);
+    case 128: return launch<IN_I8, OUT, TA, TB, 128, 128>(p, s);
+    case 64: return launch<IN_I8, OUT, TA, TB, 64, 64>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int OUT>
+static hipError_t by_layout(bool ta, bool tb, int tile, const Params &p, hipStream_t s) {
+    if (!ta && !tb) return by_tile<OUT, false, false>(tile, p, s);
+    if (!ta && tb) return by_tile<OUT, false, true>(tile, p, s);
+    if (ta && !tb) return by_tile<OUT, true, false>(tile, p, s);
+    return by_tile<OUT, true, true>(tile, p, s);
+}
+
+hipError_t launch_i8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s) {
+    if (out == OUT_I32) return by_layout<OUT_I32>(ta, tb, tile, p, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mpg

@@ -1,0 +1,227 @@
+// mpgemm_api.hip -- host side of the C ABI declared in include/mpgemm.h: argument checks,
+// handles, tile choice and kernel dispatch.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <new>
+#include <set>
+#include <string.h>
+
+#include "mpgemm.h"
+#include "mpgemm_kernel.hpp"
+
+struct mpgemm_handle_s {
+    int device;
+    int num_cus;
+};
+
+namespace {
+
+std::mutex g_handles_mu;
+std::set<mpgemm_handle_t> g_handles;  // live handles; lets destroyed ones be recognised
+
+bool handle_live(mpgemm_handle_t h) {
+    std::lock_guard<std::mutex> lock(g_handles_mu);
+    return g_handles.count(h) != 0;
+}
+
+int elem_bytes(mpgemm_dtype_t t) {
+    switch (t) {
+    case MPGEMM_R_16F:
+    case MPGEMM_R_16BF: return 2;
+    case MPGEMM_R_8I: return 1;
+    case MPGEMM_R_32F:
+    case MPGEMM_R_32I: return 4;
+    }
+    return 0;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Kernel output kind for a supported type combination, or -1.
+int out_kind(mpgemm_dtype_t a, mpgemm_dtype_t b, mpgemm_dtype_t c, mpgemm_dtype_t compute) {
+    if (a != b) return -1;
+    if (a == MPGEMM_R_16F && compute == MPGEMM_R_32F) {
+        if (c == MPGEMM_R_32F) return mpg::OUT_F32;
+        if (c == MPGEMM_R_16F) return mpg::OUT_F16;
+    }
+    if (a == MPGEMM_R_16BF && compute == MPGEMM_R_32F) {
+        if (c == MPGEMM_R_32F) return mpg::OUT_F32;
+        if (c == MPGEMM_R_16BF) return mpg::OUT_BF16;
+    }
+    if (a == MPGEMM_R_8I && compute == MPGEMM_R_32I && c == MPGEMM_R_32I) return mpg::OUT_I32;
+    return -1;
+}
+
+bool valid_dtype(int t) { return t >= MPGEMM_R_16F && t <= MPGEMM_R_32I; }
+
+// Tile edge: 256 x 256 when that still gives most CUs a tile, else smaller.
+int pick_tile(int64_t m, int64_t n) {
+    const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
+    if (t256 >= 192) return 256;
+    const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
+    if (t128 >= 96) return 128;
+    return 64;
+}
+
+bool beta_is_zero(const void *beta, mpgemm_dtype_t compute) {
+    if (compute == MPGEMM_R_32I) return *(const int32_t *)beta == 0;
+    float b;
+    memcpy(&b, beta, sizeof b);
+    return b == 0.0f;  // -0 counts as zero; NaN does not
+}
+
+}  // namespace
+
+extern "C" {
+
+mpgemm_status_t mpgemm_check(mpgemm_op_t transa, mpgemm_op_t transb, int64_t m, int64_t n,
+                             int64_t k, const void *alpha, const void *A, mpgemm_dtype_t a_type,
+                             int64_t lda, const void *B, mpgemm_dtype_t b_type, int64_t ldb,
+                             const void *beta, const void *C, mpgemm_dtype_t c_type, int64_t ldc,
+                             const void *D, mpgemm_dtype_t compute_type) {
+    if ((transa != MPGEMM_OP_N && transa != MPGEMM_OP_T) ||
+        (transb != MPGEMM_OP_N && transb != MPGEMM_OP_T))
+        return MPGEMM_STATUS_INVALID_VALUE;
+    if (m < 0 || n < 0 || k < 0) return MPGEMM_STATUS_INVALID_VALUE;
+    if (!alpha || !beta) return MPGEMM_STATUS_INVALID_VALUE;
+    if (!valid_dtype(a_type) || !valid_dtype(b_type) || !valid_dtype(c_type) ||
+        !valid_dtype(compute_type))
+        return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (out_kind(a_type, b_type, c_type, compute_type) < 0) return MPGEMM_STATUS_NOT_SUPPORTED;
+    const bool ta = transa == MPGEMM_OP_T, tb = transb == MPGEMM_OP_T;
+    const int64_t min_lda = ta ? m : k, min_ldb = tb ? k : n, min_ldc = n;
+    if (lda < (min_lda > 1 ? min_lda : 1) || ldb < (min_ldb > 1 ? min_ldb : 1) ||
+        ldc < (min_ldc > 1 ? min_ldc : 1))
+        return MPGEMM_STATUS_INVALID_VALUE;
+    if (m == 0 || n == 0) return MPGEMM_STATUS_SUCCESS;  // nothing to do, nothing is read
+    const bool read_c = !beta_is_zero(beta, compute_type);
+    if (!D) return MPGEMM_STATUS_INVALID_VALUE;
+    if (k > 0 && (!A || !B)) return MPGEMM_STATUS_INVALID_VALUE;
+    if (read_c && !C) return MPGEMM_STATUS_INVALID_VALUE;
+    // sizes the kernel indexes with 32-bit integers
+    if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return MPGEMM_STATUS_NOT_SUPPORTED;
+    const int64_t tiles = ((m + 63) / 64) * ((n + 63) / 64);
+    if (tiles > INT32_MAX) return MPGEMM_STATUS_NOT_SUPPORTED;
+    // alignment contract
+    const int ea = elem_bytes(a_type), ec = elem_bytes(c_type);
+    if (!aligned16(D) || (read_c && !aligned16(C))) return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (k > 0 && (!aligned16(A) || !aligned16(B))) return MPGEMM_STATUS_NOT_SUPPORTED;
+    if ((lda * ea) % 16 || (ldb * ea) % 16 || (ldc * ec) % 16) return MPGEMM_STATUS_NOT_SUPPORTED;
+    // every buffer offset the kernel forms spans at most 256 rows of one operand
+    const int64_t limit = (int64_t)1 << 31;
+    if (256 * lda * ea > limit - 4096 || 256 * ldb * ea > limit - 4096 || 256 * ldc * ec > limit - 4096)
+        return MPGEMM_STATUS_NOT_SUPPORTED;
+    return MPGEMM_STATUS_SUCCESS;
+}
+
+mpgemm_status_t mpgemm_create(mpgemm_handle_t *handle) {
+    if (!handle) return MPGEMM_STATUS_INVALID_VALUE;
+    *handle = nullptr;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return MPGEMM_STATUS_NO_DEVICE;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MPGEMM_STATUS_NO_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MPGEMM_STATUS_NO_DEVICE;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MPGEMM_STATUS_NO_DEVICE;
+    mpgemm_handle_t h = new (std::nothrow) mpgemm_handle_s;
+    if (!h) return MPGEMM_STATUS_ALLOC_FAILED;
+    h->device = dev;
+    h->num_cus = prop.multiProcessorCount;
+    {
+        std::lock_guard<std::mutex> lock(g_handles_mu);
+        g_handles.insert(h);
+    }
+    *handle = h;
+    return MPGEMM_STATUS_SUCCESS;
+}
+
+mpgemm_status_t mpgemm_destroy(mpgemm_handle_t handle) {
+    {
+        std::lock_guard<std::mutex> lock(g_handles_mu);
+        if (!handle || g_handles.erase(handle) == 0) return MPGEMM_STATUS_NOT_INITIALIZED;
+    }
+    delete handle;
+    return MPGEMM_STATUS_SUCCESS;
+}
+
+mpgemm_status_t mpgemm_run(mpgemm_handle_t handle, mpgemm_op_t transa, mpgemm_op_t transb,
+                           int64_t m, int64_t n, int64_t k, const void *alpha,
+                           const void *A, mpgemm_dtype_t a_type, int64_t lda,
+                           const void *B, mpgemm_dtype_t b_type, int64_t ldb,
+                           const void *beta, const void *C, mpgemm_dtype_t c_type, int64_t ldc,
+                           void *D, mpgemm_dtype_t compute_type, void *stream) {
+    if (!handle || !handle_live(handle)) return MPGEMM_STATUS_NOT_INITIALIZED;
+    const mpgemm_status_t st = mpgemm_check(transa, transb, m, n, k, alpha, A, a_type, lda, B,
+                                            b_type, ldb, beta, C, c_type, ldc, D, compute_type);
+    if (st != MPGEMM_STATUS_SUCCESS) return st;
+    if (m == 0 || n == 0) return MPGEMM_STATUS_SUCCESS;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MPGEMM_STATUS_INTERNAL_ERROR;
+    if (dev != handle->device) return MPGEMM_STATUS_WRONG_DEVICE;
+
+    mpg::Params p;
+    p.A = A;
+    p.B = B;
+    p.D = D;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.m = (int)m;
+    p.n = (int)n;
+    p.k = (int)k;
+    p.read_c = beta_is_zero(beta, compute_type) ? 0 : 1;
+    p.C = p.read_c ? C : nullptr;
+    p.alpha_f = p.beta_f = 0.0f;
+    p.alpha_i = p.beta_i = 0;
+    if (compute_type == MPGEMM_R_32I) {
+        p.alpha_i = *(const int32_t *)alpha;
+        p.beta_i = *(const int32_t *)beta;
+    } else {
+        memcpy(&p.alpha_f, alpha, sizeof(float));
+        memcpy(&p.beta_f, beta, sizeof(float));
+    }
+    const int tile = pick_tile(m, n);
+    p.tiles_m = (int)((m + tile - 1) / tile);
+    p.tiles_n = (int)((n + tile - 1) / tile);
+    const int out = out_kind(a_type, b_type, c_type, compute_type);
+    const bool ta = transa == MPGEMM_OP_T, tb = transb == MPGEMM_OP_T;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    switch (a_type) {
+    case MPGEMM_R_16F: e = mpg::launch_f16(out, ta, tb, tile, p, s); break;
+    case MPGEMM_R_16BF: e = mpg::launch_bf16(out, ta, tb, tile, p, s); break;
+    case MPGEMM_R_8I: e = mpg::launch_i8(out, ta, tb, tile, p, s); break;
+    default: return MPGEMM_STATUS_INTERNAL_ERROR;
+    }
+    return e == hipSuccess ? MPGEMM_STATUS_SUCCESS : MPGEMM_STATUS_LAUNCH_FAILED;
+}
+
+const char *mpgemm_status_string(mpgemm_status_t status) {
+    switch (status) {
+    case MPGEMM_STATUS_SUCCESS: return "success";
+    case MPGEMM_STATUS_NOT_INITIALIZED: return "handle not initialized or already destroyed";
+    case MPGEMM_STATUS_INVALID_VALUE: return "invalid value (null pointer, negative size or leading dimension too small)";
+    case MPGEMM_STATUS_NOT_SUPPORTED: return "not supported (type combination, alignment or stride outside the contract)";
+    case MPGEMM_STATUS_ALLOC_FAILED: return "host allocation failed";
+    case MPGEMM_STATUS_NO_DEVICE: return "no gfx950 HIP device";
+    case MPGEMM_STATUS_LAUNCH_FAILED: return "kernel launch failed";
+    case MPGEMM_STATUS_INTERNAL_ERROR: return "internal error";
+    case MPGEMM_STATUS_WRONG_DEVICE: return "current HIP device is not the handle's device";
+    }
+    return "unknown status";
+}
+
+mpgemm_status_t mpgemm_tile_shape(int64_t m, int64_t n, int *tile_m, int *tile_n) {
+    if (m < 0 || n < 0 || !tile_m || !tile_n) return MPGEMM_STATUS_INVALID_VALUE;
+    const int t = pick_tile(m, n);
+    *tile_m = t;
+    *tile_n = t;
+    return MPGEMM_STATUS_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+"""Helpers shared by the GPU tests: run one workload through the C-ABI on the GPU and
+compare against the oracle (full output or sampled points)."""
+import sys
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+import mixed_precision_dense_amd as mp
+import oracle
+from gemm_inputs import ELEM_BYTES, Inputs, Workload, generate, sample_points
+
+GUARD_ROWS = 2
+SENTINEL = 0x5A
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class GpuResult:
+    D: np.ndarray           # m x ldc raw storage of the output type
+    guard_ok: bool          # sentinel rows after D and the ld padding untouched
+
+
+_handle = None
+
+
+def handle():
+    global _handle
+    if _handle is None:
+        _handle = mp.Handle()
+    return _handle
+
+
+def run_gpu(inp: Inputs, d_init: Optional[np.ndarray] = None, in_place: bool = False,
+            repeat: int = 1) -> GpuResult:
+    """Run inp's workload; D is allocated with GUARD_ROWS extra rows filled with a sentinel
+    byte (or from d_init); with in_place=True D aliases C."""
+    w = inp.w
+    ob = ELEM_BYTES[w.out_type]
+    dA = mp.device_buffer(inp.A, w.in_type)
+    dB = mp.device_buffer(inp.B, w.in_type)
+    d_bytes = (w.m + GUARD_ROWS) * w.ldc * ob
+    if in_place:
+        assert inp.C is not None
+        cbuf = np.concatenate([inp.C.view(np.uint8).reshape(-1),
+                               np.full(GUARD_ROWS * w.ldc * ob, SENTINEL, np.uint8)])
+        dC = mp.device_buffer(cbuf, "i8")
+        dD = dC
+    else:
+        dC = mp.device_buffer(inp.C, w.out_type) if inp.C is not None else None
+        if d_init is not None:
+            dD = mp.device_buffer(d_init, w.out_type)
+        else:
+            dD = torch.full((d_bytes,), SENTINEL, dtype=torch.uint8, device="cuda")
+    compute = "i32" if w.in_type == "i8" else "f32"
+    alpha = int(w.alpha) if compute == "i32" else w.alpha
+    beta = int(w.beta) if compute == "i32" else w.beta
+    for _ in range(repeat):
+        mp.mpgemm_run(handle().h, w.transa, w.transb, w.m, w.n, w.k, alpha, dA, w.in_type,
+                      w.lda, dB, w.in_type, w.ldb, beta, dC, w.out_type, w.ldc, dD, compute)
+    torch.cuda.synchronize()
+    raw = dD.cpu().numpy()
+    D = raw[: w.m * w.ldc * ob].view(np.uint8)
+    guard_ok = True
+    if d_init is None:
+        guard_ok = bool(np.all(raw[w.m * w.ldc * ob:] == SENTINEL))
+        if w.ldc > w.n:
+            pad = D.reshape(w.m, w.ldc * ob)[:, w.n * ob:]
+            if in_place:
+                cpad = inp.C.view(np.uint8).reshape(w.m, w.ldc * ob)[:, w.n * ob:]
+                guard_ok &= bool(np.array_equal(pad, cpad))
+            else:
+                guard_ok &= bool(np.all(pad == SENTINEL))
+    storage = {"f16": np.uint16, "bf16": np.uint16, "f32": np.float32, "i32": np.int32}[w.out_type]
+    return GpuResult(D=D.view(storage).reshape(w.m, w.ldc), guard_ok=guard_ok)
+
+
+def oracle_ref(inp: Inputs, points=None):
+    w = inp.w
+    if w.in_type == "i8":
+        return oracle.gemm_int(w.transa, w.transb, w.m, w.n, w.k, int(w.alpha), inp.A, w.lda,
+                               inp.B, w.ldb, int(w.beta), inp.C, w.ldc, points=points)
+    return oracle.gemm_fp(w.transa, w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda,
+                          inp.B, w.in_type, w.ldb, w.beta, inp.C, w.out_type, w.ldc,
+                          points=points)
+
+
+def compare(inp: Inputs, res: GpuResult, exact: bool = False, points=None,
+            underflow_floor: bool = False):
+    """Compare the GPU output with the oracle; returns a CheckReport."""
+    w = inp.w
+    ref = oracle_ref(inp, points)
+    D = res.D[:, : w.n]
+    if points is not None:
+        D = D[points[0], points[1]]
+    if w.in_type == "i8":
+        return oracle.check_int(np.ascontiguousarray(D), ref)
+    return oracle.check_fp(np.ascontiguousarray(D), w.out_type, ref, w.k, w.alpha, exact=exact,
+                           underflow_floor=underflow_floor)
+
+
+def check_case(w: Workload, exact: bool = False, sample: Optional[int] = None, seed=None,
+               inp: Optional[Inputs] = None, in_place: bool = False):
+    say(f"[gpu case] {w.name} {w.in_type}->{w.out_type} m={w.m} n={w.n} k={w.k} "
+        f"ta={w.transa} tb={w.transb} lda={w.lda} ldb={w.ldb} ldc={w.ldc} "
+        f"alpha={w.alpha} beta={w.beta} exact={exact} sample={sample}")
+    if inp is None:
+        inp = generate(w, seed=seed)
+    res = run_gpu(inp, in_place=in_place)
+    points = None if sample is None else sample_points(w.m, w.n, sample)
+    rep = compare(inp, res, exact=exact, points=points)
+    return rep, res

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle on the same seeded
+inputs.  INT8 and exactly representable FP cases must match bit for bit; other FP results
+must sit inside the FP32 accumulation bound of the oracle's comparator."""
+import numpy as np
+import pytest
+import torch
+
+from gemm_inputs import WORKLOADS, Workload, generate, place, sample_points
+import oracle
+from tests.gpu_harness import check_case, compare, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
+
+
+def _assert(rep, res=None):
+    assert rep.ok, f"{rep.n_bad}/{rep.n} bad; worst ratio {rep.worst_ratio:.3g}; {rep.detail}"
+    if res is not None:
+        assert res.guard_ok, "D guard band or ld padding was overwritten"
+
+
+# ----------------------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("in_type", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_identity_times_b_is_b(in_type, ta, tb):
+    m = n = k = 96 if in_type != "i8" else 160
+    out = "i32" if in_type == "i8" else "f32"
+    w = Workload(f"identity_{in_type}", in_type, out, m, n, k, transa=ta, transb=tb,
+                 a_dist="zeros", b_dist="int_uniform(-100,100)" if in_type == "i8" else "uniform(-4,4)",
+                 seed=40)
+    inp = generate(w)
+    eye = np.eye(k)
+    if in_type == "i8":
+        inp.A[:, :k] = eye.astype(np.int8)
+    else:
+        from gemm_inputs import to_storage
+        inp.A[:, :k] = to_storage(eye, in_type)                # symmetric: same for ta
+    rep, res = check_case(w, exact=True, inp=inp)
+    _assert(rep, res)
+
+
+@pytest.mark.parametrize("k", [1, 7, 64, 1000, 2049, 2051])
+def test_all_ones_gives_k_exactly(k):
+    # FP16 output: K = 2049 and 2051 are RNE ties at FP16 precision (2048 and 2052)
+    w = Workload(f"ones_k{k}", "f16", "f16", 40, 72, k, a_dist="ones", b_dist="ones", seed=41)
+    rep, res = check_case(w, exact=True)
+    _assert(rep, res)
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (True, True)])
+def test_k1_fp16_exhaustive_products(ta, tb):
+    """Every FP16 pattern times a set of B values, K = 1 (the k tail masks 7 padding NaNs per
+    row): each product is exact in FP32, so D must equal the oracle bit for bit, subnormal
+    inputs included."""
+    bvals = np.array([1.0, -1.0, 0.5, 1.5, 2.0 ** -10, 2.0 ** -14, 2.0 ** -24, 3 * 2.0 ** -24,
+                      65504.0, -65504.0, 0.0, 1000.0, 0.333251953125, 7.0, -3.25, 2.0 ** 15])
+    w = Workload("k1_f16_all", "f16", "f32", 65536, bvals.size, 1, transa=ta, transb=tb, seed=60)
+    inp = generate(w)
+    patterns = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    if ta:
+        inp.A[0, :65536] = patterns
+    else:
+        inp.A[:, 0] = patterns
+    from gemm_inputs import f64_to_f16_bits
+    bbits = f64_to_f16_bits(bvals)
+    if tb:
+        inp.B[:, 0] = bbits
+    else:
+        inp.B[0, : bvals.size] = bbits
+    rep, res = check_case(w, exact=True, inp=inp)
+    _assert(rep, res)
+
+
+def test_k1_int8_product_table():
+    w = Workload("k1_i8_table", "i8", "i32", 256, 256, 1, a_dist="zeros", b_dist="zeros", seed=61)
+    inp = generate(w)
+    vals = np.arange(-128, 128).astype(np.int8)
+    inp.A[:, 0] = vals
+    inp.B[0, :256] = vals
+    rep, res = check_case(w, exact=True, inp=inp)
+    _assert(rep, res)
+
+
+# ----------------------------------------------------------------------------- ragged sweep
+RAGGED = [1, 2, 7, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+@pytest.mark.parametrize("in_type", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_ragged_sweep_exact(in_type, ta, tb):
+    """Integer-valued inputs (exact in FP32 accumulation) over ragged m, n, k; padded ld."""
+    rng = np.random.default_rng(hash((in_type, ta, tb)) % 2 ** 32)
+    out = {"f16": "f32", "bf16": "f32", "i8": "i32"}[in_type]
+    align = 16 if in_type == "i8" else 8
+    for t in range(14):
+        m, n, k = (int(x) for x in rng.choice(RAGGED, 3))
+        if t == 0:
+            m, n, k = 257, 255, 129
+        pad = lambda v: ((v + align - 1) // align) * align + align * int(rng.integers(0, 2))
+        lda = pad(m if ta else k)
+        ldb = pad(k if tb else n)
+        ldc = ((n + 3) // 4) * 4 + 4 * int(rng.integers(0, 2))
+        dist = "int_uniform(-128,127)" if in_type == "i8" else "int_uniform(-8,8)"
+        beta = float(rng.choice([0.0, 1.0, -2.0]))
+        w = Workload(f"ragged_{in_type}", in_type, out, m, n, k, transa=ta, transb=tb,
+                     alpha=float(rng.choice([1.0, 2.0, -0.5])) if in_type != "i8" else int(rng.choice([1, 3, -2])),
+                     beta=beta if in_type != "i8" else int(beta),
+                     a_dist=dist, b_dist=dist, c_dist="int_uniform(-50,50)",
+                     lda=lda, ldb=ldb, ldc=ldc, seed=1000 + t)
+        rep, res = check_case(w, exact=True)
+        _assert(rep, res)
+
+
+@pytest.mark.parametrize("in_type,out_type", [("f16", "f32"), ("f16", "f16"), ("bf16", "f32"),
+                                              ("bf16", "bf16")])
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_random_within_bound(in_type, out_type, ta, tb):
+    """Normal-distributed inputs over shapes spanning several tiles with ragged tails."""
+    for (m, n, k) in [(300, 200, 333), (513, 771, 1000), (64, 64, 4095)]:
+        w = Workload(f"rand_{in_type}_{out_type}", in_type, out_type, m, n, k, transa=ta,
+                     transb=tb, alpha=1.0, beta=0.5, a_dist="normal(0,1)", b_dist="normal(0,1)",
+                     c_dist="normal(0,1)", seed=7 + m)
+        rep, res = check_case(w)
+        _assert(rep, res)
+
+
+# ----------------------------------------------------------------------------- the five workloads
+def test_workload_fp16_256_nn_beta1_full():
+    rep, res = check_case(WORKLOADS["f16_256_nn_beta1"])
+    _assert(rep, res)
+    say(f"  worst error / bound = {rep.worst_ratio:.4f}")
+
+
+def test_workload_fp16_4096_nt_sampled():
+    rep, res = check_case(WORKLOADS["f16_4096_nt"], sample=3000)
+    _assert(rep, res)
+    say(f"  worst error / bound = {rep.worst_ratio:.4f}")
+
+
+def test_workload_fp16_4096_nt_exact_integer_valued():
+    w = WORKLOADS["f16_4096_nt"]
+    w = Workload(w.name + "_int", w.in_type, w.out_type, w.m, w.n, w.k, transa=w.transa,
+                 transb=w.transb, a_dist="int_uniform(-2,2)", b_dist="int_uniform(-2,2)", seed=w.seed)
+    rep, res = check_case(w, exact=True, sample=3000)
+    _assert(rep, res)
+
+
+def test_workload_bf16_8192_nn_sampled():
+    rep, res = check_case(WORKLOADS["bf16_8192_nn"], sample=1500)
+    _assert(rep, res)
+    say(f"  worst error / bound = {rep.worst_ratio:.4f}")
+
+
+def test_workload_int8_4096_nn_sampled_and_in_place_beta1():
+    w = WORKLOADS["i8_4096_nn"]
+    rep, res = check_case(w, sample=4000)
+    _assert(rep, res)
+    # beta = 1 with C = 0 and D written over C in place: identical bits
+    w1 = Workload(w.name + "_beta1", w.in_type, w.out_type, w.m, w.n, w.k, alpha=1, beta=1,
+                  a_dist=w.a_dist, b_dist=w.b_dist, c_dist="zeros", seed=w.seed)
+    inp1 = generate(w1)
+    res1 = run_gpu(inp1, in_place=True)
+    assert np.array_equal(res1.D[:, : w.n], res.D[:, : w.n])
+    assert res1.guard_ok
+
+
+def test_workload_fp16_ragged_f16out_sampled():
+    for name in ("f16_5000x3000x1000_f16out", "f16_5000x3000x1000_f16out_padded"):
+        rep, res = check_case(WORKLOADS[name], sample=4000)
+        _assert(rep, res)
+        say(f"  {name}: worst error / bound = {rep.worst_ratio:.4f}")
+
+
+def test_workload_fp16_ragged_exact_full():
+    w = WORKLOADS["f16_5000x3000x1000_f16out_padded"]
+    w = Workload(w.name + "_int", "f16", "f16", w.m, w.n, w.k, a_dist="int_uniform(-2,2)",
+                 b_dist="int_uniform(-2,2)", lda=w.lda, ldb=w.ldb, ldc=w.ldc, seed=5)
+    rep, res = check_case(w, exact=True, sample=20000)
+    _assert(rep, res)
+
+
+# ----------------------------------------------------------------------------- special values
+def test_nan_inf_propagation_and_beta_zero_ignores_c():
+    w = Workload("special", "f16", "f32", 70, 90, 130, beta=0.0, a_dist="uniform(-1,1)",
+                 b_dist="uniform(-1,1)", seed=50)
+    inp = generate(w, c_when_beta_zero=True)
+    inp.A[3, 5] = 0x7E00       # NaN: row 3 all NaN
+    inp.A[10, :] = 0           # row 10: zero times inf below -> NaN where B has inf
+    inp.B[7, 11] = 0x7C00      # +inf in column 11
+    inp.A[20, :] = 0x3C00      # row 20 all ones -> +inf in column 11
+    inp.B[:, 11] = np.where(np.arange(w.k) == 7, 0x7C00, 0x3C00)
+    inp.C[...] = np.float32(np.nan)  # never read with beta = 0
+    res = run_gpu(inp)
+    rep = compare(inp, res)
+    _assert(rep, res)
+    D = res.D[:, : w.n]
+    assert np.all(np.isnan(D[3])) and np.isnan(D[10, 11]) and D[20, 11] == np.inf
+    assert np.isfinite(np.delete(D[0], 11)).all()
+
+
+def test_k_zero_gives_beta_c():
+    w = Workload("k0", "f16", "f32", 33, 65, 0, alpha=1.0, beta=2.0, c_dist="uniform(-1,1)", seed=51)
+    rep, res = check_case(w, exact=True)
+    _assert(rep, res)
+    w = Workload("k0b0", "bf16", "bf16", 33, 65, 0, alpha=1.0, beta=0.0, seed=52)
+    rep, res = check_case(w, exact=True)
+    _assert(rep, res)
+
+
+def test_in_place_d_equals_c():
+    w = Workload("inplace", "bf16", "f32", 300, 260, 200, alpha=1.0, beta=0.5, ldc=264,
+                 a_dist="normal(0,1)", b_dist="normal(0,1)", c_dist="normal(0,1)", seed=53)
+    rep, res = check_case(w, in_place=True)
+    _assert(rep, res)
+
+
+def test_page_accumulator_vector_within_bound():
+    """The numerics page's K = 3 vector (section 2.2.1) through the GPU: within the bound."""
+    w = Workload("p4vec", "f16", "f32", 1, 1, 3, seed=54)
+    inp = generate(w)
+    inp.A[0, :3] = [0x3E00, 0x0002, 0x0001]      # 1.5, 2^-23, 2^-24 (FP16 subnormals)
+    inp.B[:3, 0] = [0x3E00, 0x3C00, 0x3C00]      # 1.5, 1, 1
+    res = run_gpu(inp)
+    rep = compare(inp, res)
+    _assert(rep, res)
+
+
+def test_determinism_bitwise():
+    w = Workload("det", "f16", "f32", 1000, 1000, 2000, transb=True, a_dist="normal(0,1)",
+                 b_dist="normal(0,1)", seed=55)
+    inp = generate(w)
+    first = run_gpu(inp).D.copy()
+    for _ in range(3):
+        again = run_gpu(inp, repeat=3).D
+        assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
