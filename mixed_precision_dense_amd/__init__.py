@@ -59,7 +59,7 @@ def load() -> ctypes.CDLL:
         lib.mpgemm_status_string.restype = ctypes.c_char_p
         lib.mpgemm_status_string.argtypes = [i32]
         lib.mpgemm_tile_shape.restype = i32
-        lib.mpgemm_tile_shape.argtypes = [i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        lib.mpgemm_tile_shape.argtypes = [i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         _lib = lib
     return _lib
 
@@ -142,9 +142,9 @@ def mpgemm_check(transa, transb, m, n, k, alpha, A, a_type, lda, B, b_type, ldb,
                                ctypes.byref(be), _ptr(C), _dtype(c_type), ldc, _ptr(D), ct)
 
 
-def mpgemm_tile_shape(m: int, n: int) -> tuple:
+def mpgemm_tile_shape(m: int, n: int, a_type="f16") -> tuple:
     tm, tn = ctypes.c_int(), ctypes.c_int()
-    st = load().mpgemm_tile_shape(m, n, ctypes.byref(tm), ctypes.byref(tn))
+    st = load().mpgemm_tile_shape(m, n, _dtype(a_type), ctypes.byref(tm), ctypes.byref(tn))
     if st != SUCCESS:
         raise MpgemmError(st, "mpgemm_tile_shape")
     return tm.value, tn.value
@@ -178,10 +178,6 @@ class Handle:
 
 
 # ----------------------------------------------------------------------------- buffers
-_TORCH_STORAGE = {"f16": torch.int16, "bf16": torch.int16, "i8": torch.int8,
-                  "f32": torch.float32, "i32": torch.int32}
-
-
 def device_buffer(host_array, fmt: str, device="cuda", extra_bytes: int = 0):
     """Copy raw host storage (a numpy array) to a new device tensor holding the same bytes.
 

@@ -1,8 +1,34 @@
 // Instances of the GEMM kernel for bf16 inputs (one translation unit per input type so the
-// instances compile in parallel).
+// instances compile in parallel).  Every kernel is instantiated explicitly: host code that
+// only reaches a kernel through an inlined launcher does not reliably emit its launch stub.
 #include "mpgemm_kernel.hpp"
 
 namespace mpg {
+
+template __global__ void gemm_kernel<IN_BF16, OUT_F32, false, false, 256, 256>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_F32, false, false, 128, 128>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_F32, false, false, 64, 64>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_F32, false, true, 256, 256>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_F32, false, true, 128, 128>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_F32, false, true, 64, 64>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_F32, true, false, 256, 256>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_F32, true, false, 128, 128>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_F32, true, false, 64, 64>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_F32, true, true, 256, 256>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_F32, true, true, 128, 128>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_F32, true, true, 64, 64>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_BF16, false, false, 256, 256>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_BF16, false, false, 128, 128>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_BF16, false, false, 64, 64>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_BF16, false, true, 256, 256>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_BF16, false, true, 128, 128>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_BF16, false, true, 64, 64>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_BF16, true, false, 256, 256>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_BF16, true, false, 128, 128>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_BF16, true, false, 64, 64>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_BF16, true, true, 256, 256>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_BF16, true, true, 128, 128>(Params);
+template __global__ void gemm_kernel<IN_BF16, OUT_BF16, true, true, 64, 64>(Params);
 
 template <int OUT, bool TA, bool TB>
 static hipError_t by_tile(int tile, const Params &p, hipStream_t s) {

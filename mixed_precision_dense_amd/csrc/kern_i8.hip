@@ -1,15 +1,24 @@
 // Instances of the GEMM kernel for i8 inputs (one translation unit per input type so the
-// instances compile in parallel).
+// instances compile in parallel).  Every kernel is instantiated explicitly: host code that
+// only reaches a kernel through an inlined launcher does not reliably emit its launch stub.
 #include "mpgemm_kernel.hpp"
 
 namespace mpg {
+
+template __global__ void gemm_kernel<IN_I8, OUT_I32, false, false, 256, 256>(Params);
+template __global__ void gemm_kernel<IN_I8, OUT_I32, false, false, 128, 128>(Params);
+template __global__ void gemm_kernel<IN_I8, OUT_I32, false, true, 256, 256>(Params);
+template __global__ void gemm_kernel<IN_I8, OUT_I32, false, true, 128, 128>(Params);
+template __global__ void gemm_kernel<IN_I8, OUT_I32, true, false, 256, 256>(Params);
+template __global__ void gemm_kernel<IN_I8, OUT_I32, true, false, 128, 128>(Params);
+template __global__ void gemm_kernel<IN_I8, OUT_I32, true, true, 256, 256>(Params);
+template __global__ void gemm_kernel<IN_I8, OUT_I32, true, true, 128, 128>(Params);
 
 template <int OUT, bool TA, bool TB>
 static hipError_t by_tile(int tile, const Params &p, hipStream_t s) {
     switch (tile) {
     case 256: return launch<IN_I8, OUT, TA, TB, 256, 256>(p, s);
     case 128: return launch<IN_I8, OUT, TA, TB, 128, 128>(p, s);
-    case 64: return launch<IN_I8, OUT, TA, TB, 64, 64>(p, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -55,12 +55,13 @@ int out_kind(mpgemm_dtype_t a, mpgemm_dtype_t b, mpgemm_dtype_t c, mpgemm_dtype_
 
 bool valid_dtype(int t) { return t >= MPGEMM_R_16F && t <= MPGEMM_R_32I; }
 
-// Tile edge: 256 x 256 when that still gives most CUs a tile, else smaller.
-int pick_tile(int64_t m, int64_t n) {
+// Tile edge: 256 x 256 when that still gives most CUs a tile, else smaller.  INT8 tiles are
+// at least 128 wide (a transposed INT8 operand is staged in 128-column groups).
+int pick_tile(int64_t m, int64_t n, bool int8) {
     const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
     if (t256 >= 192) return 256;
     const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
-    if (t128 >= 96) return 128;
+    if (t128 >= 96 || int8) return 128;
     return 64;
 }
 
@@ -185,7 +186,7 @@ mpgemm_status_t mpgemm_run(mpgemm_handle_t handle, mpgemm_op_t transa, mpgemm_op
         memcpy(&p.alpha_f, alpha, sizeof(float));
         memcpy(&p.beta_f, beta, sizeof(float));
     }
-    const int tile = pick_tile(m, n);
+    const int tile = pick_tile(m, n, a_type == MPGEMM_R_8I);
     p.tiles_m = (int)((m + tile - 1) / tile);
     p.tiles_n = (int)((n + tile - 1) / tile);
     const int out = out_kind(a_type, b_type, c_type, compute_type);
@@ -216,9 +217,10 @@ const char *mpgemm_status_string(mpgemm_status_t status) {
     return "unknown status";
 }
 
-mpgemm_status_t mpgemm_tile_shape(int64_t m, int64_t n, int *tile_m, int *tile_n) {
+mpgemm_status_t mpgemm_tile_shape(int64_t m, int64_t n, mpgemm_dtype_t a_type, int *tile_m,
+                                  int *tile_n) {
     if (m < 0 || n < 0 || !tile_m || !tile_n) return MPGEMM_STATUS_INVALID_VALUE;
-    const int t = pick_tile(m, n);
+    const int t = pick_tile(m, n, a_type == MPGEMM_R_8I);
     *tile_m = t;
     *tile_n = t;
     return MPGEMM_STATUS_SUCCESS;

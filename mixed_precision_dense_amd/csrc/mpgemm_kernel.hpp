@@ -3,8 +3,10 @@
 // One workgroup of 4 waves (256 lanes) computes a BM x BN tile of D.  The waves form a 2 x 2
 // grid; each owns a (BM/2) x (BN/2) sub-tile made of 32 x 32 MFMA blocks whose accumulators
 // stay in registers for the whole K loop.  K is walked in stages of 128 bytes per row (64
-// FP16/BF16 elements or 128 INT8 elements): each stage is copied from global memory into one
-// of two LDS buffers while the waves multiply out of the other one.
+// FP16/BF16 elements or 128 INT8 elements, four MFMA k steps).  Stages are copied from global
+// memory straight into two LDS buffers by direct-to-LDS buffer loads (whole 128-byte lines
+// per row), spread over the MFMAs of the stage before, while the waves multiply out of the
+// other buffer.
 //
 // The structure follows the pages' description of a tensor-core GEMM, re-planned for CDNA4:
 //   * the product is a sum of rank-k slabs, each slab an outer product of a column panel of
@@ -12,7 +14,7 @@
 //   * slabs are staged in on-chip shared memory in a block tile, each wave multiplying
 //     fragments of it ("The CUDA Handbook" section 17.5, Listing 17-5 and the paragraph after
 //     it, which also observes that the wait for the next slab's global load becomes the
-//     bottleneck -- hence the double buffer here);
+//     bottleneck -- hence the double buffer filled while the other is multiplied here);
 //   * the accumulator starts at zero, the K loop accumulates in place, and the epilogue scales
 //     the product by alpha and adds beta * C element by element before storing
 //     ("Programming Tensor Cores in CUDA 9", sections "Inner loop" and "Finishing");
@@ -25,27 +27,30 @@
 // 16-byte k chunk l / 32 of the 32-byte k step.  Accumulator register r of lane l holds
 // row 8*(r/4) + 4*(l/32) + r%4, column l % 32 of the 32 x 32 block.
 //
-// LDS layout.  Each operand tile is a row of 4 KB sub-tiles, one per 32-row (A) or
+// LDS layout.  Each operand's stage is a row of 4 KB sub-tiles, one per 32-row (A) or
 // 32-column (B) MFMA block, so that every fragment address differs between blocks only by an
 // immediate offset.
 //   * K-contiguous operand (A with transa = N, B with transb = T): sub-tile = 32 rows x 128 B.
 //     16-byte chunk c of row r sits at chunk position c ^ s(r), s(r) = (r & 7) ^ ((r >> 3) & 1),
-//     so that the 32 rows of a ds_read_b128 spread over all banks for both 8- and 16-lane
-//     LDS cycles.
+//     so that the 32 rows of a ds_read_b128 spread over all banks for both 8- and 16-lane LDS
+//     cycles.
 //   * MN-contiguous operand (A with transa = T, B with transb = N): the tile keeps its global
-//     orientation (k rows, 32 elements of m or n per sub-tile row: 64 B for 16-bit, 32 B for
-//     8-bit types) and is transposed on the way out of LDS by ds_read_b64_tr_b16 /
-//     ds_read_b64_tr_b8.  Within a 16-lane group these return, to lane t, element s of the
-//     row read by lane 4s + t/4 (b16) or 2s + t/8 (b8), at position t % 4 (t % 8) of that row.
-//     Chunk c of k-row k sits at c ^ L(k): L(k) = 2 * ((k >> 1) & 1) for 16-bit types,
-//     (k >> 2) & 1 for 8-bit types.
+//     orientation, as k-rows of 128-byte column groups (two 32-column blocks for 16-bit
+//     types, four for 8-bit types), and is transposed on the way out of LDS by
+//     ds_read_b64_tr_b16 / ds_read_b64_tr_b8.  Within a 16-lane group these return, to lane
+//     t, element s of the row read by lane 4s + t/4 (b16) or 2s + t/8 (b8), at position t % 4
+//     (t % 8) of that row.  Chunk c of k-row k sits at c ^ w(k): w(k) = 2 (k & 3) for 16-bit
+//     types, k & 7 for 8-bit types.
+//   One direct-to-LDS load of a wave fills 1 KB of LDS, lane l the 16 bytes at l * 16; the
+//   lane-to-chunk mapping applies the swizzle on the global side.
 //
-// Edges: full tiles and full K stages take an unchecked path; a tile that crosses m or n, or
-// the last stage when K is not a multiple of the stage, takes the checked path (a wave-uniform
-// branch inside the same kernel).  Out-of-range chunks are fetched with a buffer offset
-// beyond the resource's range, which the hardware returns as zero; a chunk that straddles K
-// has its elements past K zeroed, so both operands are exactly zero beyond K and no NaN can
-// leak in from padding.  Stores outside m x n are dropped the same way.
+// Edges: chunks outside m, n or K are fetched with a buffer offset beyond the resource's
+// range, which the hardware returns as zero, so out-of-range rows and columns multiply as
+// zeros.  When K is not a multiple of the 16-byte chunk, the chunks that straddle K are
+// patched in LDS after they land (elements past K zeroed), so both operands are exactly zero
+// beyond K and no NaN can leak in from padding.  Stores outside m x n are dropped the same
+// way.  All of this is the same kernel: the interior and edge tiles share every instruction
+// but a few per-lane selects.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -82,8 +87,9 @@ struct Params {
 };
 
 constexpr int kThreads = 256;
-constexpr int kStageKBytes = 128;   // bytes of k per row per stage
+constexpr int kStageKBytes = 128;   // bytes of k per row per stage (four MFMA k steps)
 constexpr int kSubTileBytes = 4096; // 32 rows x 128 B, or the transposed equivalent
+constexpr int kBuffers = 2;         // LDS double buffer
 constexpr int kGroupM = 4;          // tile-row grouping for L2 reuse
 constexpr uint32_t kOobOffset = 0x80000000u;  // a buffer offset past every resource's range
 constexpr int kNumRecords = 0x7FFFFFFF;
@@ -94,8 +100,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
                                              0x00020000);
 }
 
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+// The same raw-buffer descriptor as four dwords, for the direct-to-LDS load below.
+__device__ __forceinline__ i32x4 make_rsrc_words(const void *base) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);   // stride 0, no swizzle
+    r[2] = kNumRecords;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes [voff + soff, +16) of the buffer go
+// to LDS address m0 + 16 l.  Written as inline assembly so that the compiler does not treat it
+// as an LDS store: otherwise it would make every later transposed LDS read wait for all of
+// these loads.  The kernel orders them itself: vmcnt waits before each barrier that publishes
+// the data, and before any LDS access to it.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
+                 : "memory");
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima): at most N of this wave's
+// vector-memory loads are still in flight -- loads complete in order, so every older one has
+// landed (for direct-to-LDS loads: its data is in LDS).  The compiler does not insert this
+// wait for LDS-destination loads before a barrier by itself.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N & 0x30) << 10));
 }
 
 // Zero the bytes of a 16-byte chunk at and beyond byte `nbytes` (0..16).
@@ -110,153 +145,157 @@ __device__ __forceinline__ u32x4 keep_first_bytes(u32x4 v, int nbytes) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Operand tile: global -> registers -> LDS copy, and LDS -> MFMA fragment reads.
+// Operand stage: global -> LDS copy and LDS -> MFMA fragment reads.
 //   EB: element bytes (2 or 1).  KC: K-contiguous storage.  NS: number of 32-wide sub-tiles.
 // ---------------------------------------------------------------------------------------
 template <int EB, bool KC, int NS>
 struct Operand {
-    static constexpr int kTileBytes = NS * kSubTileBytes;
-    static constexpr int kChunkElems = 16 / EB;             // elements per 16-byte chunk
-    static constexpr int kStageK = kStageKBytes / EB;       // k elements per stage
-    // MN-contiguous geometry
-    static constexpr int kRowBytes = 32 * EB;               // one k-row of a sub-tile
-    static constexpr int kChunksPerRow = kRowBytes / 16;    // 4 (16-bit) or 2 (8-bit)
-    static constexpr int kLanesPerSub = 64 / NS;            // lanes per sub-tile per load
-    static constexpr int kRowsPerLoad = kLanesPerSub / kChunksPerRow;
     static_assert(NS == 2 || NS == 4 || NS == 8, "sub-tile count");
+    static constexpr int kStageBytes = NS * kSubTileBytes;
+    static constexpr int kChunkElems = 16 / EB;             // elements per 16-byte chunk
+    static constexpr int kSlots = NS;                       // 1 KB loads per wave per stage
+    static constexpr int kStageK = kStageKBytes / EB;       // k elements per stage
+    // MN-contiguous geometry: k-rows of 128-byte column groups, kGroupBlocks 32-wide blocks
+    // each (2 for 16-bit, 4 for 8-bit types), so that every direct load moves whole lines.
+    static constexpr int kGroupBlocks = 128 / (32 * EB);
+    static constexpr int kGroupBytes = kStageK * 128;       // one column group of a stage
+    static constexpr int kSlotsPerGroup = kStageK / 32;     // 2 (16-bit) or 4 (8-bit)
+    static_assert(KC || NS >= kGroupBlocks, "transposed operand needs whole column groups");
 
-    // Per-thread copy state.
-    uint32_t g_off0;    // global byte offset of slot 0, relative to the stage base
-    uint32_t g_slot;    // global byte stride between slots
-    uint32_t l_off0;    // LDS byte offset of slot 0 within the operand tile
-    int mn0_idx;        // slot-0 index along m/n within the tile (K-contig: row; MN: chunk start)
-    int k0_idx;         // slot-0 index along k within the stage (K-contig: chunk start; MN: row)
-    uint32_t r_off[4];  // fragment read offsets (K-contig: one per k step; MN: one, plus steps)
+    // Load slot i of wave w writes 1 KB at i * 4096 + w * 1024 of the operand's stage, lane l
+    // the 16 bytes at l * 16: for a K-contiguous operand quarter w of sub-tile i (8 rows x
+    // 128 B), for an MN-contiguous one rows 32 (i % kSlotsPerGroup) + 8 w .. + 7 of column
+    // group i / kSlotsPerGroup.
+    uint32_t g_off0;    // global byte offset of this lane's slot-0 chunk from the stage base
+    uint32_t g_slot;    // K-contig: global byte stride between slots (32 rows)
+    uint32_t row_bytes; // ld * element size
+    uint32_t l_off0;    // LDS byte offset of this lane's slot-0 chunk within the stage
+    int mn0_idx;        // m/n index (within the tile) of the slot-0 chunk's first element
+    int k0_idx;         // k index (within the stage) of the slot-0 chunk's first element
+    int slots_ok;       // slots whose chunk starts inside m/n (set per tile)
+    uint32_t r_off[4];  // fragment read offsets (K-contig: per k step; MN: per block in group)
 
-    static constexpr uint32_t kLdsSlot = KC ? kSubTileBytes : 4u * kRowsPerLoad * kRowBytes;
+    // global offset added for slot i (uniform), and the slot's first m/n and k indices
+    __device__ __forceinline__ uint32_t slot_soff(int i) const {
+        if constexpr (KC) return i * g_slot;
+        else return (uint32_t)(i % kSlotsPerGroup) * 32u * row_bytes + (uint32_t)(i / kSlotsPerGroup) * 128u;
+    }
+    static __device__ __forceinline__ int slot_mn(int i) { return KC ? 32 * i : (i / kSlotsPerGroup) * (128 / EB); }
+    static __device__ __forceinline__ int slot_k(int i) { return KC ? 0 : 32 * (i % kSlotsPerGroup); }
 
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld) {
-        const uint32_t row_bytes = (uint32_t)(ld * EB);
+        row_bytes = (uint32_t)(ld * EB);
+        l_off0 = (uint32_t)(wave * 1024 + lane * 16);
         if constexpr (KC) {
-            const int r = wave * 8 + lane / 8;                      // row within sub-tile 0
-            const int c = (lane % 8) ^ (lane / 8) ^ (wave & 1);     // logical chunk
+            const int r = wave * 8 + lane / 8;                      // row within the sub-tile
+            const int c = (lane % 8) ^ (lane / 8) ^ (wave & 1);     // logical chunk: phys ^ s(r)
             mn0_idx = r;
             k0_idx = c * kChunkElems;
             g_off0 = (uint32_t)r * row_bytes + 16u * c;
             g_slot = 32u * row_bytes;
-            l_off0 = (uint32_t)(wave * 1024 + lane * 16);
-            // fragment reads: lane reads row lane%32, chunk 2*kk + lane/32, swizzled
             const int rr = lane % 32;
-            const int sw = (rr & 7) ^ ((rr >> 3) & 1);
+            const int swr = (rr & 7) ^ ((rr >> 3) & 1);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                r_off[kk] = (uint32_t)(rr * 128 + 16 * ((2 * kk + lane / 32) ^ sw));
+                r_off[kk] = (uint32_t)(rr * 128 + 16 * ((2 * kk + lane / 32) ^ swr));
         } else {
-            const int st = lane / kLanesPerSub;
-            const int within = lane % kLanesPerSub;
-            const int kr = wave * kRowsPerLoad + within / kChunksPerRow;  // k-row of slot 0
-            const int phys = within % kChunksPerRow;
-            const int L = (EB == 2) ? 2 * ((kr >> 1) & 1) : ((kr >> 2) & 1);
-            const int c = phys ^ L;
-            mn0_idx = st * 32 + c * kChunkElems;
+            const int kr = wave * 8 + lane / 8;                     // k-row of slot 0
+            const int c = (lane % 8) ^ mn_swz(kr);                  // logical chunk in the group
+            mn0_idx = c * kChunkElems;
             k0_idx = kr;
-            g_off0 = (uint32_t)kr * row_bytes + (uint32_t)(st * kRowBytes + 16 * c);
-            g_slot = 4u * kRowsPerLoad * row_bytes;
-            l_off0 = (uint32_t)(st * kSubTileBytes + kr * kRowBytes + 16 * phys);
-            // transposed fragment reads (h = 0 half; steps add immediates)
+            g_off0 = (uint32_t)kr * row_bytes + 16u * c;
+            g_slot = 0;
             const int g = lane / 16, u = lane % 16;
             if constexpr (EB == 2) {
+                // tr16: lane u of group g reads row 8 (g >> 1) + u / 4 (+4 for the high half),
+                // 8 bytes at column 16 (g & 1) + 4 (u % 4) of its 32-column block
                 const int k = 8 * (g >> 1) + (u >> 2);
-                const int cc = 2 * (g & 1) + ((u & 3) >> 1);
-                const int Lr = 2 * ((u >> 3) & 1);
-                r_off[0] = (uint32_t)(k * kRowBytes + 16 * (cc ^ Lr) + 8 * (u & 1));
+                const int f = mn_swz(k);
+#pragma unroll
+                for (int pb = 0; pb < 2; ++pb) {
+                    const int c2 = 4 * pb + 2 * (g & 1) + ((u & 3) >> 1);
+                    r_off[pb] = (uint32_t)(k * 128 + 16 * (c2 ^ f) + 8 * (u & 1));
+                }
+                r_off[2] = r_off[3] = 0;
             } else {
+                // tr8: lane u of group g reads row 16 (g >> 1) + u / 2 (+8 for the high half),
+                // 8 bytes at column 16 (g & 1) + 8 (u % 2) of its 32-column block
                 const int k = 16 * (g >> 1) + (u >> 1);
-                const int cc = g & 1;
-                const int Lr = (u >> 3) & 1;
-                r_off[0] = (uint32_t)(k * kRowBytes + 16 * (cc ^ Lr) + 8 * (u & 1));
+                const int f = mn_swz(k);
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) {
+                    const int c2 = 2 * pb + (g & 1);
+                    r_off[pb] = (uint32_t)(k * 128 + 16 * (c2 ^ f) + 8 * (u & 1));
+                }
             }
-            r_off[1] = r_off[2] = r_off[3] = 0;
         }
     }
 
-    // Per-tile validity of this thread's chunks along m/n: K-contiguous chunks are valid for
-    // slots below `slots_ok`; MN-contiguous chunks are all valid or all invalid.
-    int slots_ok;
+    // Chunk swizzle of an MN-contiguous k-row (chunk c of row k sits at c ^ mn_swz(k)).
+    static __device__ __forceinline__ int mn_swz(int k) { return EB == 2 ? 2 * (k & 3) : (k & 7); }
 
     __device__ __forceinline__ void set_tile(int mn_left) {
         if constexpr (KC) {
-            const int rows = mn_left - mn0_idx;  // valid rows at or after slot 0's row
-            slots_ok = rows <= 0 ? 0 : min(NS, (rows + 31) / 32);
+            const int span = mn_left - mn0_idx;   // slot i starts at mn0_idx + 32 i
+            slots_ok = span <= 0 ? 0 : min(kSlots, (span + 31) / 32);
         } else {
-            slots_ok = mn0_idx < mn_left ? NS : 0;
+            const int span = mn_left - mn0_idx;   // group j starts at mn0_idx + (128 / EB) j
+            const int groups = span <= 0 ? 0 : (span + (128 / EB) - 1) / (128 / EB);
+            slots_ok = min(kSlots, groups * kSlotsPerGroup);
         }
     }
 
-    // Fetch this thread's NS chunks of one stage; `base` is the stage's start in global memory
-    // and k_left the number of valid k elements from the stage start (<= 0 past the end).
-    // Invalid chunks are fetched from beyond the buffer resource's range and arrive as zero.
-    __device__ __forceinline__ void fetch(const char *base, u32x4 (&v)[NS], int k_left) const {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-        if constexpr (KC) {
-            const bool k_ok = k_left - k0_idx > 0;
+    // Queue this lane's chunks of one stage straight into LDS.  `base` is the stage's start
+    // in global memory, k_left the valid k elements from the stage start (<= 0 past the end).
+    // Chunks outside the matrix are fetched from beyond the buffer resource's range; the
+    // hardware returns them as zero, so LDS receives zeros.
+    __device__ __forceinline__ void fetch_lds(const char *base, lds_char *stage, int wave, int k_left) const {
+        const i32x4 rs = make_rsrc_words(base);
 #pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                const uint32_t voff = (k_ok && i < slots_ok) ? g_off0 : kOobOffset;
-                v[i] = buf_load16(rs, voff, i * g_slot);
+        for (int i = 0; i < kSlots; ++i) fetch_slot(rs, stage, wave, k_left, i);
+    }
+
+    // Queue one load slot (same contract as fetch_lds; rs made from the stage base).
+    __device__ __forceinline__ void fetch_slot(i32x4 rs, lds_char *stage, int wave, int k_left, int i) const {
+        const bool ok = (k_left - (k0_idx + slot_k(i)) > 0) && i < slots_ok;
+        const uint32_t lds = (uint32_t)(uintptr_t)(stage + wave * 1024 + i * 4096);
+        dma16(rs, ok ? g_off0 : kOobOffset, slot_soff(i), lds);
+    }
+
+    // After a stage whose K boundary falls inside a 16-byte chunk has landed: zero the
+    // elements past K in the K-contiguous chunks that straddle it (MN-contiguous chunks hold
+    // one k each and are already zero past K).
+    __device__ __forceinline__ void fix_k_tail(lds_char *stage, int k_left) const {
+        if constexpr (KC) {
+            const int kvalid = k_left - k0_idx;
+            if (kvalid > 0 && kvalid < kChunkElems) {
+#pragma unroll
+                for (int i = 0; i < kSlots; ++i) {
+                    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+                    lds_u32x4 *q = (lds_u32x4 *)(stage + i * 4096 + l_off0);
+                    *q = keep_first_bytes(*q, kvalid * EB);
+                }
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                const bool ok = i < slots_ok && k0_idx + i * 4 * kRowsPerLoad < k_left;
-                v[i] = buf_load16(rs, ok ? g_off0 : kOobOffset, i * g_slot);
-            }
         }
     }
 
-    // K-contiguous chunks that straddle K get their elements past K zeroed (only ever needed
-    // in the last stage; the caller branches on that, uniformly).
-    __device__ __forceinline__ void mask_k_tail(u32x4 (&v)[NS], int k_left) const {
+    // 16-byte MFMA operand for 32-wide block `blk` at k step `kk` (0 .. 3) of a stage.
+    __device__ __forceinline__ u32x4 frag(const lds_char *stage, int blk, int kk) const {
         if constexpr (KC) {
-            const int nbytes = min(max(k_left - k0_idx, 0), kChunkElems) * EB;
-#pragma unroll
-            for (int i = 0; i < NS; ++i) v[i] = keep_first_bytes(v[i], nbytes);
-        }
-    }
-
-    // Write the fetched chunks to LDS.
-    __device__ __forceinline__ void stash(lds_char *tile, const u32x4 (&v)[NS]) const {
-#pragma unroll
-        for (int i = 0; i < NS; ++i)
-            *(__attribute__((address_space(3))) u32x4 *)(tile + l_off0 + i * kLdsSlot) = v[i];
-    }
-
-    // 16-byte MFMA operand for 32-wide block `blk` at k step `kk` (0..3).
-    __device__ __forceinline__ u32x4 frag(const lds_char *tile, int blk, int kk) const {
-        if constexpr (KC) {
-            return *(const __attribute__((address_space(3))) u32x4 *)(tile + blk * kSubTileBytes + r_off[kk]);
+            return *(const __attribute__((address_space(3))) u32x4 *)(stage + blk * kSubTileBytes + r_off[kk]);
         } else if constexpr (EB == 2) {
             typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-            const lds_char *p = tile + blk * kSubTileBytes + r_off[0] + kk * 16 * kRowBytes;
-            i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
-            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * kRowBytes));
-            u32x4 r;
-            r[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-            r[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-            r[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-            r[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-            return r;
+            const lds_char *p = stage + (blk / 2) * kGroupBytes + r_off[blk % 2] + kk * 16 * 128;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * 128));
+            // register concatenation only: no arithmetic waits on the reads here
+            return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
             typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-            const lds_char *p = tile + blk * kSubTileBytes + r_off[0] + kk * 32 * kRowBytes;
-            i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(p));
-            i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(p + 8 * kRowBytes));
-            u32x4 r;
-            r[0] = (uint32_t)lo[0];
-            r[1] = (uint32_t)lo[1];
-            r[2] = (uint32_t)hi[0];
-            r[3] = (uint32_t)hi[1];
-            return r;
+            const lds_char *p = stage + (blk / 4) * kGroupBytes + r_off[blk % 4] + kk * 32 * 128;
+            const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(p));
+            const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(p + 8 * 128));
+            return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
         }
     }
 };
@@ -331,38 +370,6 @@ template <> struct Out<OUT_I32> {
     }
 };
 
-// Instruction interleaving hints for one stage (sched_group_barrier masks: 0x008 MFMA,
-// 0x100 LDS read, 0x020 global read).  Before the barrier: k steps 0..2, each step's MFMAs
-// with the next step's fragment reads spread over its first half and the next stage's global
-// loads spread over step 0 (the LDS writes of the next stage follow).  After the barrier:
-// k step 3 with the next stage's first fragment reads.
-template <int I, int N, int W, int R, int L>
-__device__ __forceinline__ void sched_interleave() {
-    if constexpr (I < N) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if constexpr (I < W) {
-            constexpr int r = (R * (I + 1)) / W - (R * I) / W;
-            constexpr int l = (L * (I + 1)) / W - (L * I) / W;
-            if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
-            if constexpr (l > 0) __builtin_amdgcn_sched_group_barrier(0x020, l, 0);
-        }
-        sched_interleave<I + 1, N, W, R, L>();
-    }
-}
-
-template <int NMFMA, int NREAD, int NLOAD>
-struct Sched {
-    static constexpr int W = NMFMA > 1 ? NMFMA / 2 : 1;
-    static __device__ __forceinline__ void compute() {
-        sched_interleave<0, NMFMA, NMFMA, NREAD, NLOAD>();
-        sched_interleave<0, NMFMA, W, NREAD, 0>();
-        sched_interleave<0, NMFMA, W, NREAD, 0>();
-    }
-    static __device__ __forceinline__ void after_barrier() {
-        sched_interleave<0, NMFMA, W, NREAD, 0>();
-    }
-};
-
 // Map a workgroup id to its (tile_m, tile_n).  Workgroups are dispatched round-robin over
 // the 8 XCDs; ids are first remapped so that each XCD receives a contiguous run of tiles,
 // and runs are laid out in groups of kGroupM tile-rows so that the tiles of one XCD share A
@@ -394,12 +401,11 @@ void gemm_kernel(Params p) {
     using OpA = Operand<EB, !TA, NSA>;
     using OpB = Operand<EB, TB, NSB>;
     using acc_t = typename Mma<IN>::acc_t;
-    constexpr int A_BYTES = OpA::kTileBytes, B_BYTES = OpB::kTileBytes;
+    constexpr int A_BYTES = OpA::kStageBytes, B_BYTES = OpB::kStageBytes;
     constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    // LDS read instructions per k step: one per K-contiguous fragment, two per transposed one
-    constexpr int kReadsPerStep = FM * (TA ? 2 : 1) + FN * (TB ? 1 : 2);
+    constexpr int kLoadsPerStage = OpA::kSlots + OpB::kSlots;   // per wave
 
-    __shared__ __attribute__((aligned(16))) char smem_raw[2 * STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) char smem_raw[kBuffers * STAGE_BYTES];
     lds_char *smem = (lds_char *)smem_raw;
 
     const int tid = threadIdx.x;
@@ -416,8 +422,10 @@ void gemm_kernel(Params p) {
     OpB opb;
     opa.init(wave, lane, p.lda);
     opb.init(wave, lane, p.ldb);
+    opa.set_tile(m_left);
+    opb.set_tile(n_left);
 
-    // Start of this tile's operand panels (bytes); stage s adds s * stage_step.
+    // Start of this tile's operand panels (bytes); stage s adds s * step.
     const char *a_panel = (const char *)p.A + (TA ? (int64_t)m0 * EB : (int64_t)m0 * p.lda * EB);
     const char *b_panel = (const char *)p.B + (TB ? (int64_t)n0 * p.ldb * EB : (int64_t)n0 * EB);
     const int64_t a_step = TA ? (int64_t)kStageK * p.lda * EB : kStageKBytes;
@@ -430,67 +438,103 @@ void gemm_kernel(Params p) {
         for (int j = 0; j < FN; ++j) acc[i][j] = acc_t{};
 
     const int nk = (p.k + kStageK - 1) / kStageK;
-    u32x4 va[NSA], vb[NSB];
-
-    opa.set_tile(m_left);
-    opb.set_tile(n_left);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto stage_lds = [&](int s) { return smem + (s & (kBuffers - 1)) * STAGE_BYTES; };
     auto fetch_stage = [&](int s) {
         const int k_left = p.k - s * kStageK;
-        opa.fetch(a_panel + s * a_step, va, k_left);
-        opb.fetch(b_panel + s * b_step, vb, k_left);
+        opa.fetch_lds(a_panel + s * a_step, stage_lds(s), wave_u, k_left);
+        opb.fetch_lds(b_panel + s * b_step, stage_lds(s) + A_BYTES, wave_u, k_left);
     };
-    auto stash_stage = [&](int s, int buf) {
-        const int k_left = p.k - s * kStageK;
-        if (k_left < kStageK) {  // wave-uniform: the partial last stage, or past the end
-            opa.mask_k_tail(va, k_left);
-            opb.mask_k_tail(vb, k_left);
+    // K not a multiple of the 16-byte chunk: the last stage's straddling chunks are patched
+    // once they have landed (wave-uniform test).
+    const int k_tail = p.k % kStageK;
+    const bool ragged_chunk = (p.k % OpA::kChunkElems) != 0;
+    auto fix_stage = [&](int s) {
+        if (ragged_chunk && s == nk - 1) {
+            wait_vmem<0>();  // this lane's chunks have landed
+            opa.fix_k_tail(stage_lds(s), k_tail);
+            opb.fix_k_tail(stage_lds(s) + A_BYTES, k_tail);
         }
-        opa.stash(smem + buf * STAGE_BYTES, va);
-        opb.stash(smem + buf * STAGE_BYTES + A_BYTES, vb);
     };
 
-    // Fragment registers: two sets, so the reads of one k step overlap the MFMAs of another.
+    // Fragment registers: two sets, one per k step of a stage.
     u32x4 fa[2][FM], fb[2][FN];
-    auto read_frags = [&](int set, const lds_char *tile, int kk) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[set][i] = opa.frag(tile, wm * FM + i, kk);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[set][j] = opb.frag(tile + A_BYTES, wn * FN + j, kk);
+    // read unit u (< FM + FN): fragment u of A, or fragment u - FM of B
+    auto read_unit = [&](int set, const lds_char *stage, int kk, int u) {
+        if (u < FM)
+            fa[set][u] = opa.frag(stage, wm * FM + u, kk);
+        else
+            fb[set][u - FM] = opb.frag(stage + A_BYTES, wn * FN + (u - FM), kk);
     };
-    auto mfmas = [&](int set) {
+    auto read_frags = [&](int set, const lds_char *stage, int kk) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int u = 0; u < FM + FN; ++u) read_unit(set, stage, kk, u);
+    };
+    // load slot l (< kLoadsPerStage) of stage s: A slots first, then B slots
+    auto load_slot = [&](int s, int l) {
+        const int k_left = p.k - s * kStageK;
+        if (l < OpA::kSlots)
+            opa.fetch_slot(make_rsrc_words(a_panel + s * a_step), stage_lds(s), wave_u, k_left, l);
+        else
+            opb.fetch_slot(make_rsrc_words(b_panel + s * b_step), stage_lds(s) + A_BYTES, wave_u, k_left, l - OpA::kSlots);
+    };
+    // One k step: MFMA idx of fragment set `set`, each followed (in its own fenced group) by
+    // read unit idx of the next k step and by an even share of the loads given to this step.
+    // The fences keep the compiler from clustering the loads, whose issue would otherwise stall
+    // behind each other in the CU's load path.
+    constexpr int kMf = FM * FN, kUnits = FM + FN;
+    auto k_step = [&](int set, const lds_char *next_stage, int next_kk, int load_stage, int l0, int nl) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = Mma<IN>::run(fa[set][i], fb[set][j], acc[i][j]);
+        for (int idx = 0; idx < kMf; ++idx) {
+            const int i = idx / FN, j = idx % FN;
+            acc[i][j] = Mma<IN>::run(fa[set][i], fb[set][j], acc[i][j]);
+            if (idx < kUnits) read_unit(set ^ 1, next_stage, next_kk, idx);
+            if (idx == kMf - 1) {
+#pragma unroll
+                for (int u = kMf; u < kUnits; ++u) read_unit(set ^ 1, next_stage, next_kk, u);
+            }
+            // loads l0 .. l0 + nl - 1 spread evenly over the step's MFMAs
+#pragma unroll
+            for (int l = 0; l < nl; ++l)
+                if ((l * kMf) / nl == idx) load_slot(load_stage, l0 + l);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
-    if (nk > 0) {
-        fetch_stage(0);
-        stash_stage(0, 0);
-    }
+    // A stage's loads are issued in two parts: the first kL3 slots during k step 3 of the stage
+    // two before (right after the barrier that frees their buffer), the rest during k steps 0
+    // and 1 of the stage before.  Spread this way the loads use about half of the CU's
+    // load-path throughput instead of saturating it, and every load has at least one k step
+    // to land before the barrier that waits for it.
+    constexpr int kL = kLoadsPerStage;
+    constexpr int kL3 = kL / 2;
+    constexpr int kLk0 = (2 * (kL - kL3) + 2) / 3;
+    constexpr int kLk1 = kL - kL3 - kLk0;
+
+    // Prologue: stage 0 and the first part of stage 1 are queued; wait for stage 0.
+    fetch_stage(0);
+#pragma unroll
+    for (int l = 0; l < kL3; ++l) load_slot(1, l);
+    wait_vmem<kL3>();
+    fix_stage(0);
     __syncthreads();
-    read_frags(0, smem, 0);
+    read_frags(0, stage_lds(0), 0);
 
-    // Stage s multiplies out of LDS buffer s % 2 while stage s + 1 is fetched into registers
-    // and written to the other buffer.  The one barrier per stage sits between k steps 2 and
-    // 3: by then every wave has read its last fragments of buffer s % 2 and written stage
-    // s + 1, so k step 3 can run while the first fragments of stage s + 1 are read.
+    // Stage s multiplies out of LDS buffer s % 2, its k steps alternating between the two
+    // fragment sets.  The one barrier per stage sits between k steps 2 and 3: before it every
+    // wave has read its last fragments of stage s (k step 3's, read during k step 2) and
+    // waited (vmcnt) for stage s + 1; after it buffer s % 2 is free for stage s + 2, and k step
+    // 3 runs while the first fragments of stage s + 1 are read.  Stages past the end fetch
+    // only out-of-range chunks: no memory traffic.
     for (int s = 0; s < nk; ++s) {
-        const lds_char *tcur = smem + (s & 1) * STAGE_BYTES;
-        const lds_char *tnxt = smem + ((s & 1) ^ 1) * STAGE_BYTES;
-        fetch_stage(s + 1);  // past the last stage every chunk is out of range: no traffic
-        read_frags(1, tcur, 1);
-        mfmas(0);
-        read_frags(0, tcur, 2);
-        mfmas(1);
-        read_frags(1, tcur, 3);
-        mfmas(0);
-        Sched<FM * FN, kReadsPerStep, NSA + NSB>::compute();
-        stash_stage(s + 1, (s & 1) ^ 1);
+        k_step(0, stage_lds(s), 1, s + 1, kL3, kLk0);
+        k_step(1, stage_lds(s), 2, s + 1, kL3 + kLk0, kLk1);
+        k_step(0, stage_lds(s), 3, s + 1, 0, 0);
+        wait_vmem<0>();  // this wave's loads of stage s + 1 have landed
+        fix_stage(s + 1);
         __syncthreads();
-        read_frags(0, tnxt, 0);
-        mfmas(1);
-        Sched<FM * FN, kReadsPerStep, NSA + NSB>::after_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        k_step(1, stage_lds(s + 1), 0, s + 2, 0, kL3);
     }
 
     // ---- epilogue: D = alpha * acc + beta * C, masked to m x n
