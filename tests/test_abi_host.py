@@ -1,0 +1,147 @@
+"""The C-ABI library on the host: it loads, exports every function include/mpgemm.h declares,
+and checks its arguments before touching a device.  CPU only (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mpgemm.h")
+
+import mixed_precision_dense_amd as mp  # noqa: E402
+
+if not os.path.exists(mp.LIB_PATH):
+    from mixed_precision_dense_amd import build as _b
+    _b.build()
+
+ST = {v: k for k, v in mp.STATUS.items()}
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mpgemm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for n in ("mpgemm_create", "mpgemm_run", "mpgemm_destroy", "mpgemm_status_string",
+              "mpgemm_check", "mpgemm_tile_shape"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mp.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    for code in range(0, 9):
+        s = mp.status_string(code)
+        assert isinstance(s, str) and len(s) > 3
+    assert "unknown" in mp.status_string(99)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="host without a GPU only")
+def test_create_without_device_returns_no_device():
+    h = ctypes.c_void_p(123)
+    assert mp.load().mpgemm_create(ctypes.byref(h)) == ST["NO_DEVICE"]
+    assert h.value is None
+    assert mp.load().mpgemm_create(None) == ST["INVALID_VALUE"]
+
+
+def test_destroy_and_run_reject_unknown_handles():
+    lib = mp.load()
+    assert lib.mpgemm_destroy(None) == ST["NOT_INITIALIZED"]
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.mpgemm_destroy(fake) == ST["NOT_INITIALIZED"]
+    assert mp.mpgemm_run(0x1000, False, False, 8, 8, 8, 1.0, 16, "f16", 8, 16, "f16", 8, 0.0,
+                         None, "f32", 8, 16, "f32", stream=0, check=False) == ST["NOT_INITIALIZED"]
+
+
+P = 1 << 20   # a 16-byte aligned fake device address (never dereferenced on the host)
+
+
+def chk(**kw):
+    a = dict(transa=False, transb=False, m=64, n=64, k=64, alpha=1.0, A=P, a_type="f16", lda=64,
+             B=P, b_type="f16", ldb=64, beta=0.0, C=None, c_type="f32", ldc=64, D=P,
+             compute_type="f32")
+    a.update(kw)
+    return mp.mpgemm_check(a["transa"], a["transb"], a["m"], a["n"], a["k"], a["alpha"], a["A"],
+                           a["a_type"], a["lda"], a["B"], a["b_type"], a["ldb"], a["beta"],
+                           a["C"], a["c_type"], a["ldc"], a["D"], a["compute_type"])
+
+
+def test_valid_problems_pass():
+    assert chk() == ST["SUCCESS"]
+    assert chk(transa=True, transb=True) == ST["SUCCESS"]
+    assert chk(a_type="bf16", b_type="bf16", c_type="bf16", ldc=64) == ST["SUCCESS"]
+    assert chk(a_type="i8", b_type="i8", c_type="i32", compute_type="i32", lda=64, ldb=64,
+               alpha=1, beta=0) == ST["SUCCESS"]
+    assert chk(c_type="f16", ldc=64) == ST["SUCCESS"]
+    # the five workloads' argument sets
+    assert chk(m=4096, n=4096, k=4096, lda=4096, ldb=4096, ldc=4096, transb=True) == ST["SUCCESS"]
+    assert chk(m=5000, n=3000, k=1000, lda=1000, ldb=3000, ldc=3000, c_type="f16") == ST["SUCCESS"]
+    assert chk(m=256, n=256, k=256, lda=256, ldb=256, ldc=256, beta=1.0, C=P) == ST["SUCCESS"]
+
+
+def test_sizes_and_nulls():
+    assert chk(m=-1) == ST["INVALID_VALUE"]
+    assert chk(k=-5) == ST["INVALID_VALUE"]
+    assert chk(m=0, A=None, B=None, D=None) == ST["SUCCESS"]          # empty output: no-op
+    assert chk(n=0) == ST["SUCCESS"]
+    assert chk(k=0, A=None, B=None, lda=8, ldb=64) == ST["SUCCESS"]    # D = beta * C
+    assert chk(k=0, A=None, B=None, lda=1, ldb=64) == ST["NOT_SUPPORTED"]  # stride still aligned
+    assert chk(A=None) == ST["INVALID_VALUE"]
+    assert chk(D=None) == ST["INVALID_VALUE"]
+    assert chk(beta=1.0, C=None) == ST["INVALID_VALUE"]                # C needed when beta != 0
+    assert chk(beta=0.0, C=None) == ST["SUCCESS"]                      # not read when beta == 0
+    assert chk(beta=float("nan"), C=None) == ST["INVALID_VALUE"]       # NaN beta reads C
+    lib = mp.load()
+    one = ctypes.c_float(1.0)
+    # null alpha / beta pointers
+    assert lib.mpgemm_check(0, 0, 8, 8, 8, None, P, 0, 8, P, 0, 8, ctypes.byref(one), None, 3, 8,
+                            P, 3) == ST["INVALID_VALUE"]
+    assert lib.mpgemm_check(0, 0, 8, 8, 8, ctypes.byref(one), P, 0, 8, P, 0, 8, None, None, 3, 8,
+                            P, 3) == ST["INVALID_VALUE"]
+    assert lib.mpgemm_check(2, 0, 8, 8, 8, ctypes.byref(one), P, 0, 8, P, 0, 8, ctypes.byref(one),
+                            P, 3, 8, P, 3) == ST["INVALID_VALUE"]    # bad transpose flag
+
+
+def test_leading_dimension_minimums():
+    assert chk(lda=56) == ST["INVALID_VALUE"]               # lda < k
+    assert chk(transa=True, m=72, lda=64) == ST["INVALID_VALUE"]   # lda < m
+    assert chk(ldb=56) == ST["INVALID_VALUE"]               # ldb < n
+    assert chk(transb=True, k=72, lda=72, ldb=64) == ST["INVALID_VALUE"]
+    assert chk(ldc=60) == ST["INVALID_VALUE"]
+
+
+def test_types_outside_the_matrix_are_not_supported():
+    assert chk(a_type="f16", b_type="bf16") == ST["NOT_SUPPORTED"]           # mixed inputs
+    assert chk(c_type="bf16") == ST["NOT_SUPPORTED"]                          # f16 in, bf16 out
+    assert chk(compute_type="i32") == ST["NOT_SUPPORTED"]
+    assert chk(a_type="i8", b_type="i8", c_type="f32", compute_type="f32") == ST["NOT_SUPPORTED"]
+    assert chk(a_type="f32", b_type="f32") == ST["NOT_SUPPORTED"]
+    assert chk(a_type=9, b_type=9) == ST["NOT_SUPPORTED"]
+
+
+def test_alignment_contract():
+    assert chk(A=P + 8) == ST["NOT_SUPPORTED"]
+    assert chk(D=P + 4) == ST["NOT_SUPPORTED"]
+    assert chk(k=60, lda=60, ldb=64) == ST["NOT_SUPPORTED"]                  # 120 B rows
+    assert chk(n=60, ldb=60, ldc=64) == ST["NOT_SUPPORTED"]
+    assert chk(ldc=66) == ST["NOT_SUPPORTED"]
+    assert chk(a_type="i8", b_type="i8", c_type="i32", compute_type="i32", alpha=1, beta=0,
+               lda=72, ldb=64) == ST["NOT_SUPPORTED"]                       # 72 B rows of int8
+    # strides whose 256 rows span 2 GiB or more
+    assert chk(lda=1 << 22, ldb=64) == ST["NOT_SUPPORTED"]
+
+
+def test_tile_shape():
+    assert mp.mpgemm_tile_shape(4096, 4096) == (256, 256)
+    assert mp.mpgemm_tile_shape(256, 256) == (64, 64)
+    assert mp.mpgemm_tile_shape(256, 256, "i8") == (128, 128)
+    assert mp.mpgemm_tile_shape(5000, 3000) == (256, 256)
