@@ -56,11 +56,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace mpg {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -86,8 +89,20 @@ struct Params {
     int read_c;  // beta != 0
 };
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1, fully expanded in
+// the source (the long MFMA sequences exceed what the unroller expands on request).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 constexpr int kThreads = 256;
-constexpr int kStageKBytes = 128;   // bytes of k per row per stage (four MFMA k steps)
+constexpr int kStageKBytes = 128;   // bytes of k per row per stage (two MFMA k steps)
+constexpr int kStepKBytes = 64;     // bytes of k per row per MFMA k step
 constexpr int kSubTileBytes = 4096; // 32 rows x 128 B, or the transposed equivalent
 constexpr int kBuffers = 2;         // LDS double buffer
 constexpr int kGroupM = 4;          // tile-row grouping for L2 reuse
@@ -146,7 +161,8 @@ __device__ __forceinline__ u32x4 keep_first_bytes(u32x4 v, int nbytes) {
 
 // ---------------------------------------------------------------------------------------
 // Operand stage: global -> LDS copy and LDS -> MFMA fragment reads.
-//   EB: element bytes (2 or 1).  KC: K-contiguous storage.  NS: number of 32-wide sub-tiles.
+//   EB: element bytes (2 or 1).  KC: K-contiguous storage.  NS: number of 32-row (A) or
+//   32-column (B) sub-tiles in the tile, i.e. 2 NS fragment blocks of 16.
 // ---------------------------------------------------------------------------------------
 template <int EB, bool KC, int NS>
 struct Operand {
@@ -155,12 +171,14 @@ struct Operand {
     static constexpr int kChunkElems = 16 / EB;             // elements per 16-byte chunk
     static constexpr int kSlots = NS;                       // 1 KB loads per wave per stage
     static constexpr int kStageK = kStageKBytes / EB;       // k elements per stage
-    // MN-contiguous geometry: k-rows of 128-byte column groups, kGroupBlocks 32-wide blocks
-    // each (2 for 16-bit, 4 for 8-bit types), so that every direct load moves whole lines.
-    static constexpr int kGroupBlocks = 128 / (32 * EB);
+    static constexpr int kStepK = kStepKBytes / EB;         // k elements per MFMA k step
+    // MN-contiguous geometry: k-rows of 128-byte column groups, kGroupBlocks 16-wide fragment
+    // blocks each (4 for 16-bit, 8 for 8-bit types), so that every direct load moves whole
+    // 128-byte lines.
+    static constexpr int kGroupBlocks = 128 / (16 * EB);
     static constexpr int kGroupBytes = kStageK * 128;       // one column group of a stage
     static constexpr int kSlotsPerGroup = kStageK / 32;     // 2 (16-bit) or 4 (8-bit)
-    static_assert(KC || NS >= kGroupBlocks, "transposed operand needs whole column groups");
+    static_assert(KC || 2 * NS >= kGroupBlocks, "transposed operand needs whole column groups");
 
     // Load slot i of wave w writes 1 KB at i * 4096 + w * 1024 of the operand's stage, lane l
     // the 16 bytes at l * 16: for a K-contiguous operand quarter w of sub-tile i (8 rows x
@@ -173,7 +191,8 @@ struct Operand {
     int mn0_idx;        // m/n index (within the tile) of the slot-0 chunk's first element
     int k0_idx;         // k index (within the stage) of the slot-0 chunk's first element
     int slots_ok;       // slots whose chunk starts inside m/n (set per tile)
-    uint32_t r_off[4];  // fragment read offsets (K-contig: per k step; MN: per block in group)
+    // fragment read offsets: K-contig per k step; MN-contig per block position in its group
+    uint32_t r_off[kGroupBlocks > 2 ? kGroupBlocks : 2];
 
     // global offset added for slot i (uniform), and the slot's first m/n and k indices
     __device__ __forceinline__ uint32_t slot_soff(int i) const {
@@ -183,21 +202,28 @@ struct Operand {
     static __device__ __forceinline__ int slot_mn(int i) { return KC ? 32 * i : (i / kSlotsPerGroup) * (128 / EB); }
     static __device__ __forceinline__ int slot_k(int i) { return KC ? 0 : 32 * (i % kSlotsPerGroup); }
 
+    // Chunk swizzle of a K-contiguous row r of a sub-tile (chunk c sits at c ^ kc_swz(r)).
+    static __device__ __forceinline__ int kc_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+    // Chunk swizzle of an MN-contiguous k-row (chunk c of row k sits at c ^ mn_swz(k)).
+    static __device__ __forceinline__ int mn_swz(int k) {
+        return EB == 2 ? 2 * ((k & 3) ^ ((k >> 3) & 1)) : ((k & 7) ^ ((k >> 4) & 1));
+    }
+
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld) {
         row_bytes = (uint32_t)(ld * EB);
         l_off0 = (uint32_t)(wave * 1024 + lane * 16);
+        const int g = lane / 16, u = lane % 16;
         if constexpr (KC) {
             const int r = wave * 8 + lane / 8;                      // row within the sub-tile
-            const int c = (lane % 8) ^ (lane / 8) ^ (wave & 1);     // logical chunk: phys ^ s(r)
+            const int c = (lane % 8) ^ kc_swz(r);                   // logical chunk of phys lane % 8
             mn0_idx = r;
             k0_idx = c * kChunkElems;
             g_off0 = (uint32_t)r * row_bytes + 16u * c;
             g_slot = 32u * row_bytes;
-            const int rr = lane % 32;
-            const int swr = (rr & 7) ^ ((rr >> 3) & 1);
+            // fragment: lane reads row u of its 16-row block, chunk g of the 64-byte k step
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                r_off[kk] = (uint32_t)(rr * 128 + 16 * ((2 * kk + lane / 32) ^ swr));
+            for (int ks = 0; ks < 2; ++ks)
+                r_off[ks] = (uint32_t)(u * 128 + 16 * ((4 * ks + g) ^ kc_swz(u)));
         } else {
             const int kr = wave * 8 + lane / 8;                     // k-row of slot 0
             const int c = (lane % 8) ^ mn_swz(kr);                  // logical chunk in the group
@@ -205,34 +231,23 @@ struct Operand {
             k0_idx = kr;
             g_off0 = (uint32_t)kr * row_bytes + 16u * c;
             g_slot = 0;
-            const int g = lane / 16, u = lane % 16;
             if constexpr (EB == 2) {
-                // tr16: lane u of group g reads row 8 (g >> 1) + u / 4 (+4 for the high half),
-                // 8 bytes at column 16 (g & 1) + 4 (u % 4) of its 32-column block
-                const int k = 8 * (g >> 1) + (u >> 2);
-                const int f = mn_swz(k);
+                // tr16: lane 4 s + q of group g reads k-row 8 g + s (+4 for the high half),
+                // 8 bytes at column 4 q of its 16-column block
+                const int s = u >> 2, q = u & 3, k = 8 * g + s;
 #pragma unroll
-                for (int pb = 0; pb < 2; ++pb) {
-                    const int c2 = 4 * pb + 2 * (g & 1) + ((u & 3) >> 1);
-                    r_off[pb] = (uint32_t)(k * 128 + 16 * (c2 ^ f) + 8 * (u & 1));
-                }
-                r_off[2] = r_off[3] = 0;
+                for (int pb = 0; pb < kGroupBlocks; ++pb)
+                    r_off[pb] = (uint32_t)(k * 128 + 16 * ((2 * pb + (q >> 1)) ^ mn_swz(k)) + 8 * (q & 1));
             } else {
-                // tr8: lane u of group g reads row 16 (g >> 1) + u / 2 (+8 for the high half),
-                // 8 bytes at column 16 (g & 1) + 8 (u % 2) of its 32-column block
-                const int k = 16 * (g >> 1) + (u >> 1);
-                const int f = mn_swz(k);
+                // tr8: lane 2 s + q of group g reads k-row 16 g + s (+8 for the high half),
+                // 8 bytes at column 8 q of its 16-column block
+                const int s = u >> 1, q = u & 1, k = 16 * g + s;
 #pragma unroll
-                for (int pb = 0; pb < 4; ++pb) {
-                    const int c2 = 2 * pb + (g & 1);
-                    r_off[pb] = (uint32_t)(k * 128 + 16 * (c2 ^ f) + 8 * (u & 1));
-                }
+                for (int pb = 0; pb < kGroupBlocks; ++pb)
+                    r_off[pb] = (uint32_t)(k * 128 + 16 * (pb ^ mn_swz(k)) + 8 * q);
             }
         }
     }
-
-    // Chunk swizzle of an MN-contiguous k-row (chunk c of row k sits at c ^ mn_swz(k)).
-    static __device__ __forceinline__ int mn_swz(int k) { return EB == 2 ? 2 * (k & 3) : (k & 7); }
 
     __device__ __forceinline__ void set_tile(int mn_left) {
         if constexpr (KC) {
@@ -279,20 +294,20 @@ struct Operand {
         }
     }
 
-    // 16-byte MFMA operand for 32-wide block `blk` at k step `kk` (0 .. 3) of a stage.
-    __device__ __forceinline__ u32x4 frag(const lds_char *stage, int blk, int kk) const {
+    // 16-byte MFMA operand of 16-wide block `blk` at k step `ks` (0 or 1) of a stage.
+    __device__ __forceinline__ u32x4 frag(const lds_char *stage, int blk, int ks) const {
         if constexpr (KC) {
-            return *(const __attribute__((address_space(3))) u32x4 *)(stage + blk * kSubTileBytes + r_off[kk]);
+            return *(const __attribute__((address_space(3))) u32x4 *)(stage + blk * 2048 + r_off[ks]);
         } else if constexpr (EB == 2) {
             typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-            const lds_char *p = stage + (blk / 2) * kGroupBytes + r_off[blk % 2] + kk * 16 * 128;
+            const lds_char *p = stage + (blk / kGroupBlocks) * kGroupBytes + r_off[blk % kGroupBlocks] + ks * kStepK * 128;
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * 128));
             // register concatenation only: no arithmetic waits on the reads here
             return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
             typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-            const lds_char *p = stage + (blk / 4) * kGroupBytes + r_off[blk % 4] + kk * 32 * 128;
+            const lds_char *p = stage + (blk / kGroupBlocks) * kGroupBytes + r_off[blk % kGroupBlocks] + ks * kStepK * 128;
             const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(p));
             const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(p + 8 * 128));
             return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
@@ -301,30 +316,43 @@ struct Operand {
 };
 
 // ---------------------------------------------------------------------------------------
-// MFMA per input type
+// MFMA per input type: one 16 x 16 block, 64 bytes of k per row (32 FP16/BF16 or 64 INT8).
+// The accumulators are pinned to the accumulation registers through the asm operand
+// constraint; every other register holds fragments, offsets and the loop state.  An
+// accumulator is next used as an input 64 (or, for smaller tiles, 16 or 4) MFMAs later, and
+// the epilogue waits out the last results (drain_mfma) before reading them.
 // ---------------------------------------------------------------------------------------
 template <int IN> struct Mma;
 template <> struct Mma<IN_F16> {
-    typedef f32x16 acc_t;
-    static __device__ __forceinline__ acc_t run(u32x4 a, u32x4 b, acc_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    typedef f32x4 acc_t;
+    static __device__ __forceinline__ void run(u32x4 a, u32x4 b, acc_t &c) {
+        asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
     }
 };
 template <> struct Mma<IN_BF16> {
-    typedef f32x16 acc_t;
-    static __device__ __forceinline__ acc_t run(u32x4 a, u32x4 b, acc_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    typedef f32x4 acc_t;
+    static __device__ __forceinline__ void run(u32x4 a, u32x4 b, acc_t &c) {
+        asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
     }
 };
 template <> struct Mma<IN_I8> {
-    typedef i32x16 acc_t;
-    static __device__ __forceinline__ acc_t run(u32x4 a, u32x4 b, acc_t c) {
-        return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
-                                                     __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+    typedef i32x4 acc_t;
+    static __device__ __forceinline__ void run(u32x4 a, u32x4 b, acc_t &c) {
+        asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
     }
 };
+
+// Wait states between the last MFMA of the loop and the first read of its results by any
+// other instruction (more than an 8-pass MFMA's result latency), then every accumulator is
+// passed through an empty volatile statement, so no read of it can be scheduled earlier.
+template <typename Acc, int FM, int FN>
+__device__ __forceinline__ void drain_mfma(Acc (&acc)[FM][FN]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
 
 // ---------------------------------------------------------------------------------------
 // Epilogue element: v = alpha * acc + beta * c, converted to the output type.
@@ -396,7 +424,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void gemm_kernel(Params p) {
     constexpr int EB = (IN == IN_I8) ? 1 : 2;
     constexpr int NSA = BM / 32, NSB = BN / 32;
-    constexpr int FM = NSA / 2, FN = NSB / 2;   // MFMA blocks per wave (2 x 2 wave grid)
+    constexpr int FM = BM / 32, FN = BN / 32;   // 16-wide MFMA blocks per wave (2 x 2 wave grid)
     constexpr int kStageK = kStageKBytes / EB;
     using OpA = Operand<EB, !TA, NSA>;
     using OpB = Operand<EB, TB, NSB>;
@@ -460,15 +488,15 @@ void gemm_kernel(Params p) {
     // Fragment registers: two sets, one per k step of a stage.
     u32x4 fa[2][FM], fb[2][FN];
     // read unit u (< FM + FN): fragment u of A, or fragment u - FM of B
-    auto read_unit = [&](int set, const lds_char *stage, int kk, int u) {
+    auto read_unit = [&](int set, const lds_char *stage, int ks, int u) {
         if (u < FM)
-            fa[set][u] = opa.frag(stage, wm * FM + u, kk);
+            fa[set][u] = opa.frag(stage, wm * FM + u, ks);
         else
-            fb[set][u - FM] = opb.frag(stage + A_BYTES, wn * FN + (u - FM), kk);
+            fb[set][u - FM] = opb.frag(stage + A_BYTES, wn * FN + (u - FM), ks);
     };
-    auto read_frags = [&](int set, const lds_char *stage, int kk) {
+    auto read_frags = [&](int set, const lds_char *stage, int ks) {
 #pragma unroll
-        for (int u = 0; u < FM + FN; ++u) read_unit(set, stage, kk, u);
+        for (int u = 0; u < FM + FN; ++u) read_unit(set, stage, ks, u);
     };
     // load slot l (< kLoadsPerStage) of stage s: A slots first, then B slots
     auto load_slot = [&](int s, int l) {
@@ -478,64 +506,60 @@ void gemm_kernel(Params p) {
         else
             opb.fetch_slot(make_rsrc_words(b_panel + s * b_step), stage_lds(s) + A_BYTES, wave_u, k_left, l - OpA::kSlots);
     };
-    // One k step: MFMA idx of fragment set `set`, each followed (in its own fenced group) by
-    // read unit idx of the next k step and by an even share of the loads given to this step.
-    // The fences keep the compiler from clustering the loads, whose issue would otherwise stall
-    // behind each other in the CU's load path.
+    // One k step: the FM x FN MFMAs of fragment set `set`, each in its own fenced group so that
+    // the compiler keeps the interleave.  The fragments of the next k step (into the other
+    // set) are read during the first kReadWindow MFMAs, so they have landed well before the
+    // next k step needs them; the `nl` load slots of stage `load_stage` start right after the
+    // barrier and are spread over the first kLoadWindow MFMAs, giving each load more than a k
+    // step to land while keeping the CU's load path from being flooded.
     constexpr int kMf = FM * FN, kUnits = FM + FN;
-    auto k_step = [&](int set, const lds_char *next_stage, int next_kk, int load_stage, int l0, int nl) {
-#pragma unroll
-        for (int idx = 0; idx < kMf; ++idx) {
-            const int i = idx / FN, j = idx % FN;
-            acc[i][j] = Mma<IN>::run(fa[set][i], fb[set][j], acc[i][j]);
-            if (idx < kUnits) read_unit(set ^ 1, next_stage, next_kk, idx);
-            if (idx == kMf - 1) {
-#pragma unroll
-                for (int u = kMf; u < kUnits; ++u) read_unit(set ^ 1, next_stage, next_kk, u);
-            }
-            // loads l0 .. l0 + nl - 1 spread evenly over the step's MFMAs
-#pragma unroll
-            for (int l = 0; l < nl; ++l)
-                if ((l * kMf) / nl == idx) load_slot(load_stage, l0 + l);
+    constexpr int kReadWindow = kMf / 2 > 0 ? kMf / 2 : 1;
+    constexpr int kLoadWindow = (3 * kMf) / 4 > 0 ? (3 * kMf) / 4 : 1;
+    auto k_step = [&](auto set_c, const lds_char *next_stage, int next_ks, int load_stage, auto nl_c) {
+        constexpr int set = decltype(set_c)::value, nl = decltype(nl_c)::value;
+        static_for<kMf>([&](auto idx_c) {
+            constexpr int idx = decltype(idx_c)::value;
+            constexpr int i = idx / FN, j = idx % FN;
+            Mma<IN>::run(fa[set][i], fb[set][j], acc[i][j]);
+            static_for<kUnits>([&](auto u_c) {
+                constexpr int u = decltype(u_c)::value;
+                if constexpr ((u * kReadWindow) / kUnits == idx) read_unit(set ^ 1, next_stage, next_ks, u);
+            });
+            static_for<nl>([&](auto l_c) {
+                constexpr int l = decltype(l_c)::value;
+                if constexpr ((l * kLoadWindow) / (nl > 0 ? nl : 1) == idx) load_slot(load_stage, l);
+            });
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using CL = std::integral_constant<int, kLoadsPerStage>;
 
-    // A stage's loads are issued in two parts: the first kL3 slots during k step 3 of the stage
-    // two before (right after the barrier that frees their buffer), the rest during k steps 0
-    // and 1 of the stage before.  Spread this way the loads use about half of the CU's
-    // load-path throughput instead of saturating it, and every load has at least one k step
-    // to land before the barrier that waits for it.
-    constexpr int kL = kLoadsPerStage;
-    constexpr int kL3 = kL / 2;
-    constexpr int kLk0 = (2 * (kL - kL3) + 2) / 3;
-    constexpr int kLk1 = kL - kL3 - kLk0;
-
-    // Prologue: stage 0 and the first part of stage 1 are queued; wait for stage 0.
+    // Prologue: stages 0 and 1 are queued; wait for stage 0.
     fetch_stage(0);
-#pragma unroll
-    for (int l = 0; l < kL3; ++l) load_slot(1, l);
-    wait_vmem<kL3>();
+    fetch_stage(1);
+    wait_vmem<kLoadsPerStage>();
     fix_stage(0);
     __syncthreads();
     read_frags(0, stage_lds(0), 0);
 
-    // Stage s multiplies out of LDS buffer s % 2, its k steps alternating between the two
-    // fragment sets.  The one barrier per stage sits between k steps 2 and 3: before it every
-    // wave has read its last fragments of stage s (k step 3's, read during k step 2) and
-    // waited (vmcnt) for stage s + 1; after it buffer s % 2 is free for stage s + 2, and k step
-    // 3 runs while the first fragments of stage s + 1 are read.  Stages past the end fetch
-    // only out-of-range chunks: no memory traffic.
+    // Stage s multiplies out of LDS buffer s % 2 in two k steps.  During k step 0 the waves
+    // read the fragments of k step 1.  Then each wave waits (vmcnt) for its loads of stage
+    // s + 1, and one barrier publishes stage s + 1 and certifies that every wave has read
+    // its last fragments of stage s.  During k step 1 the waves read the first fragments of
+    // stage s + 1 and queue the loads of stage s + 2 into the buffer just freed, so every load
+    // has at least one k step to land before the barrier that waits for it.  Stages past the
+    // end fetch only out-of-range chunks: no memory traffic.
     for (int s = 0; s < nk; ++s) {
-        k_step(0, stage_lds(s), 1, s + 1, kL3, kLk0);
-        k_step(1, stage_lds(s), 2, s + 1, kL3 + kLk0, kLk1);
-        k_step(0, stage_lds(s), 3, s + 1, 0, 0);
+        k_step(C0{}, stage_lds(s), 1, 0, C0{});
         wait_vmem<0>();  // this wave's loads of stage s + 1 have landed
         fix_stage(s + 1);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        k_step(1, stage_lds(s + 1), 0, s + 2, 0, kL3);
+        k_step(C1{}, stage_lds(s + 1), 0, s + 2, CL{});
     }
+    drain_mfma(acc);
 
     // ---- epilogue: D = alpha * acc + beta * C, masked to m x n
     constexpr int OB = Out<OUT>::kBytes;
@@ -543,12 +567,13 @@ void gemm_kernel(Params p) {
     const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.D + tile_off);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc((const char *)(p.read_c ? p.C : p.D) + tile_off);
     const uint32_t ldc_b = (uint32_t)(p.ldc * OB);
-    const int row_base = wm * (BM / 2) + 4 * (lane / 32);
-    const int col_base = wn * (BN / 2) + (lane % 32);
+    // accumulator register r of block (i, j): row 16 i + 4 (lane / 16) + r, column 16 j + lane % 16
+    const int row_base = wm * (BM / 2) + 4 * (lane / 16);
+    const int col_base = wn * (BN / 2) + (lane % 16);
     // byte offset of accumulator element r of block (i, j), or an out-of-range offset
     auto out_off = [&](int i, int j, int r) -> uint32_t {
-        const int row = row_base + i * 32 + 8 * (r / 4) + (r % 4);
-        const int col = col_base + j * 32;
+        const int row = row_base + i * 16 + r;
+        const int col = col_base + j * 16;
         const bool ok = full_mn || (row < m_left && col < n_left);
         return ok ? (uint32_t)row * ldc_b + (uint32_t)col * OB : kOobOffset;
     };
@@ -557,11 +582,11 @@ void gemm_kernel(Params p) {
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                decltype(Out<OUT>::load(rc, 0)) cv[16];
+                decltype(Out<OUT>::load(rc, 0)) cv[4];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) cv[r] = Out<OUT>::load(rc, out_off(i, j, r));
+                for (int r = 0; r < 4; ++r) cv[r] = Out<OUT>::load(rc, out_off(i, j, r));
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
+                for (int r = 0; r < 4; ++r) {
                     if constexpr (IN == IN_I8) {
                         const uint32_t v = (uint32_t)p.alpha_i * (uint32_t)acc[i][j][r] +
                                            (uint32_t)p.beta_i * (uint32_t)cv[r];
@@ -577,7 +602,7 @@ void gemm_kernel(Params p) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
+                for (int r = 0; r < 4; ++r) {
                     if constexpr (IN == IN_I8)
                         Out<OUT>::store(rd, out_off(i, j, r), (int)((uint32_t)p.alpha_i * (uint32_t)acc[i][j][r]));
                     else
