@@ -163,6 +163,15 @@ __device__ __forceinline__ u32x4 keep_first_bytes(u32x4 v, int nbytes) {
 // Operand stage: global -> LDS copy and LDS -> MFMA fragment reads.
 //   EB: element bytes (2 or 1).  KC: K-contiguous storage.  NS: number of 32-row (A) or
 //   32-column (B) sub-tiles in the tile, i.e. 2 NS fragment blocks of 16.
+//
+// Loads never leave the operand.  K-contiguous rows outside the tile's m (or n) range are
+// clamped to the last valid row and MN-contiguous chunks past the row end to its last
+// 16-byte block, so every stage but the last stays inside rows that exist.  For the last stage the buffer resource's record
+// count is the exact number of guaranteed-readable bytes from the stage start (and zero for
+// stages past K), so chunks beyond the operand's end read as zero.  Data loaded for rows or
+// columns outside m x n only reaches accumulators of outputs that are never stored.  Chunks
+// beyond K within a row are the exception -- they would reach every output -- and are zeroed
+// in LDS once they have landed (fix_k_tail).
 // ---------------------------------------------------------------------------------------
 template <int EB, bool KC, int NS>
 struct Operand {
@@ -184,23 +193,11 @@ struct Operand {
     // the 16 bytes at l * 16: for a K-contiguous operand quarter w of sub-tile i (8 rows x
     // 128 B), for an MN-contiguous one rows 32 (i % kSlotsPerGroup) + 8 w .. + 7 of column
     // group i / kSlotsPerGroup.
-    uint32_t g_off0;    // global byte offset of this lane's slot-0 chunk from the stage base
-    uint32_t g_slot;    // K-contig: global byte stride between slots (32 rows)
-    uint32_t row_bytes; // ld * element size
-    uint32_t l_off0;    // LDS byte offset of this lane's slot-0 chunk within the stage
-    int mn0_idx;        // m/n index (within the tile) of the slot-0 chunk's first element
-    int k0_idx;         // k index (within the stage) of the slot-0 chunk's first element
-    int slots_ok;       // slots whose chunk starts inside m/n (set per tile)
+    uint32_t voff[kSlots];  // per slot: byte offset of this lane's chunk from the stage start
+    uint32_t l_off0;        // LDS byte offset of this lane's slot-0 chunk within the stage
+    int k0_idx;             // K-contig: k index (within the stage) of this lane's chunks
     // fragment read offsets: K-contig per k step; MN-contig per block position in its group
     uint32_t r_off[kGroupBlocks > 2 ? kGroupBlocks : 2];
-
-    // global offset added for slot i (uniform), and the slot's first m/n and k indices
-    __device__ __forceinline__ uint32_t slot_soff(int i) const {
-        if constexpr (KC) return i * g_slot;
-        else return (uint32_t)(i % kSlotsPerGroup) * 32u * row_bytes + (uint32_t)(i / kSlotsPerGroup) * 128u;
-    }
-    static __device__ __forceinline__ int slot_mn(int i) { return KC ? 32 * i : (i / kSlotsPerGroup) * (128 / EB); }
-    static __device__ __forceinline__ int slot_k(int i) { return KC ? 0 : 32 * (i % kSlotsPerGroup); }
 
     // Chunk swizzle of a K-contiguous row r of a sub-tile (chunk c sits at c ^ kc_swz(r)).
     static __device__ __forceinline__ int kc_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -209,28 +206,33 @@ struct Operand {
         return EB == 2 ? 2 * ((k & 3) ^ ((k >> 3) & 1)) : ((k & 7) ^ ((k >> 4) & 1));
     }
 
-    __device__ __forceinline__ void init(int wave, int lane, int64_t ld) {
-        row_bytes = (uint32_t)(ld * EB);
+    // mn_left: rows (K-contig) or columns (MN-contig) of the operand from the tile's first
+    // one; at least 1.
+    __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int mn_left) {
+        const uint32_t row_bytes = (uint32_t)(ld * EB);
         l_off0 = (uint32_t)(wave * 1024 + lane * 16);
         const int g = lane / 16, u = lane % 16;
         if constexpr (KC) {
             const int r = wave * 8 + lane / 8;                      // row within the sub-tile
             const int c = (lane % 8) ^ kc_swz(r);                   // logical chunk of phys lane % 8
-            mn0_idx = r;
             k0_idx = c * kChunkElems;
-            g_off0 = (uint32_t)r * row_bytes + 16u * c;
-            g_slot = 32u * row_bytes;
+#pragma unroll
+            for (int i = 0; i < kSlots; ++i) voff[i] = (uint32_t)min(32 * i + r, mn_left - 1) * row_bytes + 16u * c;
             // fragment: lane reads row u of its 16-row block, chunk g of the 64-byte k step
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 r_off[ks] = (uint32_t)(u * 128 + 16 * ((4 * ks + g) ^ kc_swz(u)));
         } else {
-            const int kr = wave * 8 + lane / 8;                     // k-row of slot 0
+            const int kr = wave * 8 + lane / 8;                     // k-row within a 32-row slot
             const int c = (lane % 8) ^ mn_swz(kr);                  // logical chunk in the group
-            mn0_idx = c * kChunkElems;
             k0_idx = kr;
-            g_off0 = (uint32_t)kr * row_bytes + 16u * c;
-            g_slot = 0;
+            // chunks past the operand's row end (edge tiles) are clamped to its last 16-byte
+            // block, so no load runs into later rows
+            const int col_max = ((mn_left * EB + 15) & ~15) - 16;
+#pragma unroll
+            for (int i = 0; i < kSlots; ++i)
+                voff[i] = (uint32_t)(32 * (i % kSlotsPerGroup) + kr) * row_bytes +
+                          (uint32_t)min((i / kSlotsPerGroup) * 128 + 16 * c, col_max);
             if constexpr (EB == 2) {
                 // tr16: lane 4 s + q of group g reads k-row 8 g + s (+4 for the high half),
                 // 8 bytes at column 4 q of its 16-column block
@@ -249,46 +251,25 @@ struct Operand {
         }
     }
 
-    __device__ __forceinline__ void set_tile(int mn_left) {
-        if constexpr (KC) {
-            const int span = mn_left - mn0_idx;   // slot i starts at mn0_idx + 32 i
-            slots_ok = span <= 0 ? 0 : min(kSlots, (span + 31) / 32);
-        } else {
-            const int span = mn_left - mn0_idx;   // group j starts at mn0_idx + (128 / EB) j
-            const int groups = span <= 0 ? 0 : (span + (128 / EB) - 1) / (128 / EB);
-            slots_ok = min(kSlots, groups * kSlotsPerGroup);
-        }
+    // Queue load slot i of a stage: rs addresses the stage's start (record count bounded as
+    // described above), lds_stage_w is the LDS address of the stage plus 1024 * wave.
+    __device__ __forceinline__ void load(i32x4 rs, uint32_t lds_stage_w, int i) const {
+        dma16(rs, voff[i], 0u, lds_stage_w + (uint32_t)i * 4096u);
     }
 
-    // Queue this lane's chunks of one stage straight into LDS.  `base` is the stage's start
-    // in global memory, k_left the valid k elements from the stage start (<= 0 past the end).
-    // Chunks outside the matrix are fetched from beyond the buffer resource's range; the
-    // hardware returns them as zero, so LDS receives zeros.
-    __device__ __forceinline__ void fetch_lds(const char *base, lds_char *stage, int wave, int k_left) const {
-        const i32x4 rs = make_rsrc_words(base);
-#pragma unroll
-        for (int i = 0; i < kSlots; ++i) fetch_slot(rs, stage, wave, k_left, i);
-    }
-
-    // Queue one load slot (same contract as fetch_lds; rs made from the stage base).
-    __device__ __forceinline__ void fetch_slot(i32x4 rs, lds_char *stage, int wave, int k_left, int i) const {
-        const bool ok = (k_left - (k0_idx + slot_k(i)) > 0) && i < slots_ok;
-        const uint32_t lds = (uint32_t)(uintptr_t)(stage + wave * 1024 + i * 4096);
-        dma16(rs, ok ? g_off0 : kOobOffset, slot_soff(i), lds);
-    }
-
-    // After a stage whose K boundary falls inside a 16-byte chunk has landed: zero the
-    // elements past K in the K-contiguous chunks that straddle it (MN-contiguous chunks hold
-    // one k each and are already zero past K).
+    // After the last stage has landed, when K ends inside it: zero this lane's K-contiguous
+    // chunks at and past K (whole chunks past K, the tail of the chunk that straddles it).
+    // MN-contiguous k-rows past K lie beyond the operand and were read as zeros.
     __device__ __forceinline__ void fix_k_tail(lds_char *stage, int k_left) const {
         if constexpr (KC) {
             const int kvalid = k_left - k0_idx;
-            if (kvalid > 0 && kvalid < kChunkElems) {
+            if (kvalid < kChunkElems) {
+                const int keep = kvalid > 0 ? kvalid * EB : 0;
 #pragma unroll
                 for (int i = 0; i < kSlots; ++i) {
                     typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
                     lds_u32x4 *q = (lds_u32x4 *)(stage + i * 4096 + l_off0);
-                    *q = keep_first_bytes(*q, kvalid * EB);
+                    *q = keep_first_bytes(*q, keep);
                 }
             }
         }
@@ -312,6 +293,27 @@ struct Operand {
             const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(p + 8 * 128));
             return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
         }
+    }
+};
+
+// Buffer resource of one operand's stages: the address of the next stage to load and the
+// record count of the last stage (the exact number of guaranteed-readable bytes from its
+// start, computed once per tile).
+struct StageCursor {
+    uint64_t base;      // global address of the next stage's start
+    int64_t step;       // bytes between consecutive stages
+    int last_records;   // record count for the last stage
+    __device__ __forceinline__ void advance() { base += (uint64_t)step; }
+    // Resource for stage s of nk: every byte before the last stage, exact for the last
+    // stage, none past it.
+    __device__ __forceinline__ i32x4 rsrc(int s, int nk) const {
+        const int nr = s < nk - 1 ? kNumRecords : (s == nk - 1 ? last_records : 0);
+        i32x4 r;
+        r[0] = (int)(uint32_t)base;
+        r[1] = (int)((uint32_t)(base >> 32) & 0xFFFFu);   // stride 0, no swizzle
+        r[2] = nr;
+        r[3] = 0x00020000;
+        return r;
     }
 };
 
@@ -430,11 +432,15 @@ void gemm_kernel(Params p) {
     using OpB = Operand<EB, TB, NSB>;
     using acc_t = typename Mma<IN>::acc_t;
     constexpr int A_BYTES = OpA::kStageBytes, B_BYTES = OpB::kStageBytes;
-    constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     constexpr int kLoadsPerStage = OpA::kSlots + OpB::kSlots;   // per wave
 
-    __shared__ __attribute__((aligned(16))) char smem_raw[kBuffers * STAGE_BYTES];
+    // LDS: [A stage 0 | A stage 1 | B stage 0 | B stage 1].  Stage parity is a compile-time
+    // constant in the unrolled loop below, so every fragment read is one base register plus
+    // an immediate offset.
+    __shared__ __attribute__((aligned(16))) char smem_raw[kBuffers * (A_BYTES + B_BYTES)];
     lds_char *smem = (lds_char *)smem_raw;
+    auto stage_a = [&](int parity) { return smem + parity * A_BYTES; };
+    auto stage_b = [&](int parity) { return smem + kBuffers * A_BYTES + parity * B_BYTES; };
 
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64;
@@ -448,16 +454,32 @@ void gemm_kernel(Params p) {
 
     OpA opa;
     OpB opb;
-    opa.init(wave, lane, p.lda);
-    opb.init(wave, lane, p.ldb);
-    opa.set_tile(m_left);
-    opb.set_tile(n_left);
+    opa.init(wave, lane, p.lda, m_left);
+    opb.init(wave, lane, p.ldb, n_left);
 
-    // Start of this tile's operand panels (bytes); stage s adds s * step.
-    const char *a_panel = (const char *)p.A + (TA ? (int64_t)m0 * EB : (int64_t)m0 * p.lda * EB);
-    const char *b_panel = (const char *)p.B + (TB ? (int64_t)n0 * p.ldb * EB : (int64_t)n0 * EB);
-    const int64_t a_step = TA ? (int64_t)kStageK * p.lda * EB : kStageKBytes;
-    const int64_t b_step = TB ? kStageKBytes : (int64_t)kStageK * p.ldb * EB;
+    const int nk = (p.k + kStageK - 1) / kStageK;
+    const int k_tail = p.k % kStageK;
+
+    // Stage cursors.  The guaranteed-readable end of an operand stored rows x cols with
+    // leading dimension ld is the end of the 16-byte block holding its last element; the
+    // last stage's record count is the distance from its start to that end.
+    StageCursor ca, cb;
+    {
+        const int64_t ra = TA ? p.k : p.m, cla = TA ? p.m : p.k;
+        const int64_t rb = TB ? p.n : p.k, clb = TB ? p.k : p.n;
+        const int64_t end_a = (ra - 1) * p.lda * EB + ((cla * EB + 15) & ~(int64_t)15);
+        const int64_t end_b = (rb - 1) * p.ldb * EB + ((clb * EB + 15) & ~(int64_t)15);
+        const int64_t off_a = TA ? (int64_t)m0 * EB : (int64_t)m0 * p.lda * EB;
+        const int64_t off_b = TB ? (int64_t)n0 * p.ldb * EB : (int64_t)n0 * EB;
+        ca.step = TA ? (int64_t)kStageK * p.lda * EB : kStageKBytes;
+        cb.step = TB ? kStageKBytes : (int64_t)kStageK * p.ldb * EB;
+        ca.base = (uint64_t)p.A + (uint64_t)off_a;
+        cb.base = (uint64_t)p.B + (uint64_t)off_b;
+        const int64_t la = end_a - off_a - (int64_t)(nk - 1) * ca.step;
+        const int64_t lb = end_b - off_b - (int64_t)(nk - 1) * cb.step;
+        ca.last_records = (int)(la < 0 ? 0 : (la > kNumRecords ? kNumRecords : la));
+        cb.last_records = (int)(lb < 0 ? 0 : (lb > kNumRecords ? kNumRecords : lb));
+    }
 
     acc_t acc[FM][FN];
 #pragma unroll
@@ -465,69 +487,61 @@ void gemm_kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = acc_t{};
 
-    const int nk = (p.k + kStageK - 1) / kStageK;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    auto stage_lds = [&](int s) { return smem + (s & (kBuffers - 1)) * STAGE_BYTES; };
-    auto fetch_stage = [&](int s) {
-        const int k_left = p.k - s * kStageK;
-        opa.fetch_lds(a_panel + s * a_step, stage_lds(s), wave_u, k_left);
-        opb.fetch_lds(b_panel + s * b_step, stage_lds(s) + A_BYTES, wave_u, k_left);
-    };
-    // K not a multiple of the 16-byte chunk: the last stage's straddling chunks are patched
-    // once they have landed (wave-uniform test).
-    const int k_tail = p.k % kStageK;
-    const bool ragged_chunk = (p.k % OpA::kChunkElems) != 0;
-    auto fix_stage = [&](int s) {
-        if (ragged_chunk && s == nk - 1) {
+    const uint32_t lds_w = (uint32_t)(uintptr_t)smem + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
+    // K ends inside the last stage: its K-contiguous chunks past K are zeroed once they have
+    // landed (wave-uniform test).
+    auto fix_stage = [&](int s, int parity) {
+        if (k_tail != 0 && s == nk - 1) {
             wait_vmem<0>();  // this lane's chunks have landed
-            opa.fix_k_tail(stage_lds(s), k_tail);
-            opb.fix_k_tail(stage_lds(s) + A_BYTES, k_tail);
+            opa.fix_k_tail(stage_a(parity), k_tail);
+            opb.fix_k_tail(stage_b(parity), k_tail);
         }
     };
 
     // Fragment registers: two sets, one per k step of a stage.
     u32x4 fa[2][FM], fb[2][FN];
     // read unit u (< FM + FN): fragment u of A, or fragment u - FM of B
-    auto read_unit = [&](int set, const lds_char *stage, int ks, int u) {
+    auto read_unit = [&](int set, int parity, int ks, int u) {
         if (u < FM)
-            fa[set][u] = opa.frag(stage, wm * FM + u, ks);
+            fa[set][u] = opa.frag(stage_a(parity), wm * FM + u, ks);
         else
-            fb[set][u - FM] = opb.frag(stage + A_BYTES, wn * FN + (u - FM), ks);
+            fb[set][u - FM] = opb.frag(stage_b(parity), wn * FN + (u - FM), ks);
     };
-    auto read_frags = [&](int set, const lds_char *stage, int ks) {
-#pragma unroll
-        for (int u = 0; u < FM + FN; ++u) read_unit(set, stage, ks, u);
-    };
-    // load slot l (< kLoadsPerStage) of stage s: A slots first, then B slots
-    auto load_slot = [&](int s, int l) {
-        const int k_left = p.k - s * kStageK;
+    // Loads of one stage: A slots first, then B slots; rs_a / rs_b address the stage.
+    i32x4 rs_a, rs_b;
+    auto load_slot = [&](int parity, int l) {
         if (l < OpA::kSlots)
-            opa.fetch_slot(make_rsrc_words(a_panel + s * a_step), stage_lds(s), wave_u, k_left, l);
+            opa.load(rs_a, lds_w + (uint32_t)(parity * A_BYTES), l);
         else
-            opb.fetch_slot(make_rsrc_words(b_panel + s * b_step), stage_lds(s) + A_BYTES, wave_u, k_left, l - OpA::kSlots);
+            opb.load(rs_b, lds_w + (uint32_t)(kBuffers * A_BYTES + parity * B_BYTES), l - OpA::kSlots);
     };
-    // One k step: the FM x FN MFMAs of fragment set `set`, each in its own fenced group so that
-    // the compiler keeps the interleave.  The fragments of the next k step (into the other
-    // set) are read during the first kReadWindow MFMAs, so they have landed well before the
-    // next k step needs them; the `nl` load slots of stage `load_stage` start right after the
-    // barrier and are spread over the first kLoadWindow MFMAs, giving each load more than a k
-    // step to land while keeping the CU's load path from being flooded.
+    // Prepare the resources of stage s (the cursors then move to stage s + 1).
+    auto next_rsrc_a = [&](int s) { rs_a = ca.rsrc(s, nk); ca.advance(); };
+    auto next_rsrc_b = [&](int s) { rs_b = cb.rsrc(s, nk); cb.advance(); };
+    auto no_hook = [&](auto) {};
+
+    // One k step: the FM x FN MFMAs of fragment set `set`, each in its own fenced group with at
+    // most two other instructions -- a wave issues one instruction per four cycles, so more
+    // would hold back the next 16-cycle MFMA.  The fragments of the next k step (into the
+    // other set) are read at the even MFMAs of the first half; the `nl` load slots of the
+    // stage being refilled go to every (kMf / nl)-th MFMA from the second one on.
     constexpr int kMf = FM * FN, kUnits = FM + FN;
-    constexpr int kReadWindow = kMf / 2 > 0 ? kMf / 2 : 1;
-    constexpr int kLoadWindow = (3 * kMf) / 4 > 0 ? (3 * kMf) / 4 : 1;
-    auto k_step = [&](auto set_c, const lds_char *next_stage, int next_ks, int load_stage, auto nl_c) {
+    auto k_step = [&](auto set_c, int rd_parity, int rd_ks, int ld_parity, auto nl_c, auto &&hook) {
         constexpr int set = decltype(set_c)::value, nl = decltype(nl_c)::value;
         static_for<kMf>([&](auto idx_c) {
             constexpr int idx = decltype(idx_c)::value;
             constexpr int i = idx / FN, j = idx % FN;
             Mma<IN>::run(fa[set][i], fb[set][j], acc[i][j]);
+            hook(idx_c);
             static_for<kUnits>([&](auto u_c) {
                 constexpr int u = decltype(u_c)::value;
-                if constexpr ((u * kReadWindow) / kUnits == idx) read_unit(set ^ 1, next_stage, next_ks, u);
+                constexpr int at = 2 * kUnits <= kMf ? 2 * u : (u * kMf) / kUnits;
+                if constexpr (at == idx) read_unit(set ^ 1, rd_parity, rd_ks, u);
             });
             static_for<nl>([&](auto l_c) {
                 constexpr int l = decltype(l_c)::value;
-                if constexpr ((l * kLoadWindow) / (nl > 0 ? nl : 1) == idx) load_slot(load_stage, l);
+                constexpr int at = ((l * kMf) / (nl > 0 ? nl : 1) + 1) % kMf;
+                if constexpr (at == idx) load_slot(ld_parity, l);
             });
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -536,29 +550,49 @@ void gemm_kernel(Params p) {
     using C1 = std::integral_constant<int, 1>;
     using CL = std::integral_constant<int, kLoadsPerStage>;
 
-    // Prologue: stages 0 and 1 are queued; wait for stage 0.
-    fetch_stage(0);
-    fetch_stage(1);
-    wait_vmem<kLoadsPerStage>();
-    fix_stage(0);
-    __syncthreads();
-    read_frags(0, stage_lds(0), 0);
-
-    // Stage s multiplies out of LDS buffer s % 2 in two k steps.  During k step 0 the waves
+    // Stage s multiplies out of LDS buffers s % 2 in two k steps.  During k step 0 the waves
     // read the fragments of k step 1.  Then each wave waits (vmcnt) for its loads of stage
-    // s + 1, and one barrier publishes stage s + 1 and certifies that every wave has read
-    // its last fragments of stage s.  During k step 1 the waves read the first fragments of
-    // stage s + 1 and queue the loads of stage s + 2 into the buffer just freed, so every load
-    // has at least one k step to land before the barrier that waits for it.  Stages past the
-    // end fetch only out-of-range chunks: no memory traffic.
-    for (int s = 0; s < nk; ++s) {
-        k_step(C0{}, stage_lds(s), 1, 0, C0{});
+    // s + 1, and one barrier publishes stage s + 1 and certifies that every wave has read its
+    // last fragments of stage s.  During k step 1 the waves read the first fragments of stage
+    // s + 1 and queue the loads of stage s + 2 into the buffers just freed, so every load has
+    // at least one k step to land before the barrier that waits for it.
+    // The resources of stage s + 2 are prepared in odd MFMA groups of k step 0, a few scalar
+    // instructions at a time.
+    auto stage_iter = [&](int s, auto par_c) {
+        constexpr int P = decltype(par_c)::value;
+        k_step(C0{}, P, 1, 0, C0{}, [&](auto idx_c) {
+            constexpr int idx = decltype(idx_c)::value;
+            if constexpr (idx == 1 % kMf) next_rsrc_a(s + 2);
+            if constexpr (idx == 3 % kMf) next_rsrc_b(s + 2);
+        });
         wait_vmem<0>();  // this wave's loads of stage s + 1 have landed
-        fix_stage(s + 1);
+        fix_stage(s + 1, P ^ 1);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        k_step(C1{}, stage_lds(s + 1), 0, s + 2, CL{});
+        k_step(C1{}, P ^ 1, 0, P, CL{}, no_hook);
+    };
+
+    // Prologue: stages 0 and 1 are queued; wait for stage 0.
+    next_rsrc_a(0);
+    next_rsrc_b(0);
+    static_for<kLoadsPerStage>([&](auto l_c) { load_slot(0, decltype(l_c)::value); });
+    next_rsrc_a(1);
+    next_rsrc_b(1);
+    static_for<kLoadsPerStage>([&](auto l_c) { load_slot(1, decltype(l_c)::value); });
+    wait_vmem<kLoadsPerStage>();
+    fix_stage(0, 0);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) read_unit(0, 0, 0, u);
+
+    // Stages are taken in pairs (buffer parity 0, then 1).  For an odd number of stages the
+    // last pair's second stage lies past K: its loads read zero records, so it multiplies zeros
+    // into the accumulators, which leaves them unchanged.
+    for (int s = 0; s < nk; s += 2) {
+        stage_iter(s, C0{});
+        stage_iter(s + 1, C1{});
     }
+    wait_vmem<0>();  // no direct load into LDS is left in flight when the workgroup ends
     drain_mfma(acc);
 
     // ---- epilogue: D = alpha * acc + beta * C, masked to m x n
