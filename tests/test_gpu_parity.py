@@ -112,6 +112,30 @@ def test_ragged_sweep_exact(in_type, ta, tb):
         _assert(rep, res)
 
 
+# Tile-edge cases.  Shapes are chosen for the kernel's edge handling: 256 x 256 tiles (at
+# least 192 of them) whose last tile row and column are ragged, K stages ending in a partial
+# stage and odd stage counts, leading dimensions equal to the row length (what lies past K in
+# a row is the next row's data, not padding), very short rows of a transposed-read operand,
+# and tiny outputs.  Inputs are integer-valued, so every result is exact.
+EDGE_K = {"f16": (200, 136), "bf16": (200, 136), "i8": (208, 272)}   # stage tails; odd counts
+
+
+@pytest.mark.parametrize("in_type", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_tile_edges_exact(in_type, ta, tb):
+    out = "i32" if in_type == "i8" else "f32"
+    dist = "int_uniform(-128,127)" if in_type == "i8" else "int_uniform(-8,8)"
+    k1, k2 = EDGE_K[in_type]
+    shapes = [(256 * 14 + 37, 256 * 14 + 5, k1), (256 * 15 + 255, 256 * 13 + 1, k2),
+              (5, 3, k1), (300, 9, k2), (17, 260, 320), (1, 1, 1), (2, 513, 48), (257, 1, 4112)]
+    for t, (m, n, k) in enumerate(shapes):
+        w = Workload(f"edge_{in_type}", in_type, out, m, n, k, transa=ta, transb=tb,
+                     a_dist=dist, b_dist=dist, seed=3000 + t)
+        say(f"  edge case {in_type} ta={ta} tb={tb} m={m} n={n} k={k} lda={w.lda} ldb={w.ldb}")
+        rep, res = check_case(w, exact=True)
+        _assert(rep, res)
+
+
 @pytest.mark.parametrize("in_type,out_type", [("f16", "f32"), ("f16", "f16"), ("bf16", "f32"),
                                               ("bf16", "bf16")])
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
