@@ -157,8 +157,8 @@ def cpu_baseline(w, target_s: float = 15.0):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="f16_4096_nt")
     ap.add_argument("--all", action="store_true",
                     help="also time every named workload (one line each on stderr)")
