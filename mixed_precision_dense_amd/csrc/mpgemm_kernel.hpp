@@ -148,6 +148,14 @@ __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N & 0x30) << 10));
 }
 
+// s_waitcnt lgkmcnt(N) (vmcnt and expcnt left at their maxima): at most N of this wave's LDS
+// (and scalar memory) operations are still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_lds() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+}
+
 // Zero the bytes of a 16-byte chunk at and beyond byte `nbytes` (0..16).
 __device__ __forceinline__ u32x4 keep_first_bytes(u32x4 v, int nbytes) {
 #pragma unroll
@@ -208,7 +216,8 @@ struct Operand {
 
     // mn_left: rows (K-contig) or columns (MN-contig) of the operand from the tile's first
     // one; at least 1.
-    __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int mn_left) {
+    // lds_base: byte offset of this operand's stages in LDS, folded into the read offsets.
+    __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int mn_left, uint32_t lds_base) {
         const uint32_t row_bytes = (uint32_t)(ld * EB);
         l_off0 = (uint32_t)(wave * 1024 + lane * 16);
         const int g = lane / 16, u = lane % 16;
@@ -221,7 +230,7 @@ struct Operand {
             // fragment: lane reads row u of its 16-row block, chunk g of the 64-byte k step
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                r_off[ks] = (uint32_t)(u * 128 + 16 * ((4 * ks + g) ^ kc_swz(u)));
+                r_off[ks] = lds_base + (uint32_t)(u * 128 + 16 * ((4 * ks + g) ^ kc_swz(u)));
         } else {
             const int kr = wave * 8 + lane / 8;                     // k-row within a 32-row slot
             const int c = (lane % 8) ^ mn_swz(kr);                  // logical chunk in the group
@@ -239,14 +248,14 @@ struct Operand {
                 const int s = u >> 2, q = u & 3, k = 8 * g + s;
 #pragma unroll
                 for (int pb = 0; pb < kGroupBlocks; ++pb)
-                    r_off[pb] = (uint32_t)(k * 128 + 16 * ((2 * pb + (q >> 1)) ^ mn_swz(k)) + 8 * (q & 1));
+                    r_off[pb] = lds_base + (uint32_t)(k * 128 + 16 * ((2 * pb + (q >> 1)) ^ mn_swz(k)) + 8 * (q & 1));
             } else {
                 // tr8: lane 2 s + q of group g reads k-row 16 g + s (+8 for the high half),
                 // 8 bytes at column 8 q of its 16-column block
                 const int s = u >> 1, q = u & 1, k = 16 * g + s;
 #pragma unroll
                 for (int pb = 0; pb < kGroupBlocks; ++pb)
-                    r_off[pb] = (uint32_t)(k * 128 + 16 * (pb ^ mn_swz(k)) + 8 * q);
+                    r_off[pb] = lds_base + (uint32_t)(k * 128 + 16 * (pb ^ mn_swz(k)) + 8 * q);
             }
         }
     }
@@ -275,7 +284,8 @@ struct Operand {
         }
     }
 
-    // 16-byte MFMA operand of 16-wide block `blk` at k step `ks` (0 or 1) of a stage.
+    // 16-byte MFMA operand of 16-wide block `blk` at k step `ks` (0 or 1) of a stage; `stage`
+    // is the LDS start plus the stage's offset from this operand's first stage.
     __device__ __forceinline__ u32x4 frag(const lds_char *stage, int blk, int ks) const {
         if constexpr (KC) {
             return *(const __attribute__((address_space(3))) u32x4 *)(stage + blk * 2048 + r_off[ks]);
@@ -454,8 +464,8 @@ void gemm_kernel(Params p) {
 
     OpA opa;
     OpB opb;
-    opa.init(wave, lane, p.lda, m_left);
-    opb.init(wave, lane, p.ldb, n_left);
+    opa.init(wave, lane, p.lda, m_left, 0u);
+    opb.init(wave, lane, p.ldb, n_left, (uint32_t)(kBuffers * A_BYTES));
 
     const int nk = (p.k + kStageK - 1) / kStageK;
     const int k_tail = p.k % kStageK;
@@ -503,9 +513,9 @@ void gemm_kernel(Params p) {
     // read unit u (< FM + FN): fragment u of A, or fragment u - FM of B
     auto read_unit = [&](int set, int parity, int ks, int u) {
         if (u < FM)
-            fa[set][u] = opa.frag(stage_a(parity), wm * FM + u, ks);
+            fa[set][u] = opa.frag(smem + parity * A_BYTES, wm * FM + u, ks);
         else
-            fb[set][u - FM] = opb.frag(stage_b(parity), wn * FN + (u - FM), ks);
+            fb[set][u - FM] = opb.frag(smem + parity * B_BYTES, wn * FN + (u - FM), ks);
     };
     // Loads of one stage: A slots first, then B slots; rs_a / rs_b address the stage.
     i32x4 rs_a, rs_b;
@@ -528,6 +538,9 @@ void gemm_kernel(Params p) {
     constexpr int kMf = FM * FN, kUnits = FM + FN;
     auto k_step = [&](auto set_c, int rd_parity, int rd_ks, int ld_parity, auto nl_c, auto &&hook) {
         constexpr int set = decltype(set_c)::value, nl = decltype(nl_c)::value;
+        // The fragments of this k step were read during the first half of the previous one:
+        // one wait for all of them instead of a wait before each MFMA that uses a new one.
+        wait_lds<0>();
         static_for<kMf>([&](auto idx_c) {
             constexpr int idx = decltype(idx_c)::value;
             constexpr int i = idx / FN, j = idx % FN;
