@@ -1,12 +1,12 @@
 // mpgemm_kernel.hpp -- the gfx950 MFMA GEMM kernel: D = alpha * op(A) * op(B) + beta * C.
 //
-// One workgroup of 4 waves (256 lanes) computes a BM x BN tile of D.  The waves form a 2 x 2
-// grid; each owns a (BM/2) x (BN/2) sub-tile made of 32 x 32 MFMA blocks whose accumulators
-// stay in registers for the whole K loop.  K is walked in stages of 128 bytes per row (64
-// FP16/BF16 elements or 128 INT8 elements, four MFMA k steps).  Stages are copied from global
-// memory straight into two LDS buffers by direct-to-LDS buffer loads (whole 128-byte lines
-// per row), spread over the MFMAs of the stage before, while the waves multiply out of the
-// other buffer.
+// One workgroup of 4 waves (256 lanes, one wave per SIMD) computes a BM x BN tile of D.  The
+// waves form a 2 x 2 grid; each owns a (BM/2) x (BN/2) sub-tile made of 16 x 16 MFMA blocks
+// whose accumulators stay in the accumulation registers for the whole K loop.  K is walked in
+// stages of 128 bytes per row (64 FP16/BF16 or 128 INT8 elements, two MFMA k steps of 64
+// bytes).  Stages are copied from global memory straight into LDS by direct-to-LDS buffer
+// loads (whole 128-byte lines per row) into one of two buffers while the waves multiply out
+// of the other.
 //
 // The structure follows the pages' description of a tensor-core GEMM, re-planned for CDNA4:
 //   * the product is a sum of rank-k slabs, each slab an outer product of a column panel of
@@ -22,35 +22,34 @@
 //     Cores in CUDA 9", "What are Tensor Cores?"; "Mixed-Precision Programming with CUDA 8",
 //     DP4A, Figure 2).
 //
-// MFMA lane layouts used (v_mfma_f32_32x32x16_{f16,bf16}, v_mfma_i32_32x32x32_i8): every
-// operand register set is 16 bytes per lane; lane l holds row (A) or column (B) l % 32 and the
-// 16-byte k chunk l / 32 of the 32-byte k step.  Accumulator register r of lane l holds
-// row 8*(r/4) + 4*(l/32) + r%4, column l % 32 of the 32 x 32 block.
+// Why 16 x 16 blocks: on random data the chip runs power-limited, and v_mfma_f32_16x16x32_*
+// and v_mfma_i32_16x16x64_i8 do the same work as the 32 x 32 forms for 15-20 % less energy
+// (measured: higher sustained clock at equal MFMA utilisation).  Their 16-cycle issue
+// interval leaves room for two other instructions between MFMAs without delaying the next
+// one, which is what the hand-placed schedule below is built around.
 //
-// LDS layout.  Each operand's stage is a row of 4 KB sub-tiles, one per 32-row (A) or
-// 32-column (B) MFMA block, so that every fragment address differs between blocks only by an
-// immediate offset.
-//   * K-contiguous operand (A with transa = N, B with transb = T): sub-tile = 32 rows x 128 B.
-//     16-byte chunk c of row r sits at chunk position c ^ s(r), s(r) = (r & 7) ^ ((r >> 3) & 1),
-//     so that the 32 rows of a ds_read_b128 spread over all banks for both 8- and 16-lane LDS
-//     cycles.
+// MFMA lane layouts (probed on gfx950): every operand register set is 16 bytes per lane;
+// lane l holds row (A) or column (B) l % 16 and the 16-byte k chunk l / 16 of the 64-byte k
+// step.  Accumulator register r of lane l holds row 4 * (l / 16) + r, column l % 16.
+//
+// LDS layout: [A stage 0 | A stage 1 | B stage 0 | B stage 1].  Each operand's stage is a row
+// of 4 KB sub-tiles of 32 rows (K-contiguous) or a row of 128-byte column groups
+// (MN-contiguous), so that fragment addresses differ only by immediate offsets.
+//   * K-contiguous operand (A with transa = N, B with transb = T): sub-tile = 32 rows x 128 B,
+//     16-byte chunk c of row r at chunk position c ^ kc_swz(r), which keeps a fragment read
+//     free of bank conflicts (see kc_swz).
 //   * MN-contiguous operand (A with transa = T, B with transb = N): the tile keeps its global
-//     orientation, as k-rows of 128-byte column groups (two 32-column blocks for 16-bit
-//     types, four for 8-bit types), and is transposed on the way out of LDS by
+//     orientation, as k-rows of 128-byte column groups (four 16-column blocks for 16-bit
+//     types, eight for 8-bit types), and is transposed on the way out of LDS by
 //     ds_read_b64_tr_b16 / ds_read_b64_tr_b8.  Within a 16-lane group these return, to lane
 //     t, element s of the row read by lane 4s + t/4 (b16) or 2s + t/8 (b8), at position t % 4
-//     (t % 8) of that row.  Chunk c of k-row k sits at c ^ w(k): w(k) = 2 (k & 3) for 16-bit
-//     types, k & 7 for 8-bit types.
+//     (t % 8) of that row.  Chunk c of k-row k sits at c ^ mn_swz(k).
 //   One direct-to-LDS load of a wave fills 1 KB of LDS, lane l the 16 bytes at l * 16; the
 //   lane-to-chunk mapping applies the swizzle on the global side.
 //
-// Edges: chunks outside m, n or K are fetched with a buffer offset beyond the resource's
-// range, which the hardware returns as zero, so out-of-range rows and columns multiply as
-// zeros.  When K is not a multiple of the 16-byte chunk, the chunks that straddle K are
-// patched in LDS after they land (elements past K zeroed), so both operands are exactly zero
-// beyond K and no NaN can leak in from padding.  Stores outside m x n are dropped the same
-// way.  All of this is the same kernel: the interior and edge tiles share every instruction
-// but a few per-lane selects.
+// Edges are handled inside the same kernel (see the Operand comment): loads stay inside the
+// operand through clamped offsets and an exact record count for the last stage, chunks past
+// K are zeroed in LDS, and stores outside m x n are dropped through an out-of-range offset.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -207,8 +206,15 @@ struct Operand {
     // fragment read offsets: K-contig per k step; MN-contig per block position in its group
     uint32_t r_off[kGroupBlocks > 2 ? kGroupBlocks : 2];
 
-    // Chunk swizzle of a K-contiguous row r of a sub-tile (chunk c sits at c ^ kc_swz(r)).
-    static __device__ __forceinline__ int kc_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+    // Chunk swizzle of a K-contiguous row r of a sub-tile (chunk c sits at c ^ kc_swz(r)):
+    // bits 1 and 2 of (r mod 16) / 2 swapped.  A fragment read (16 rows x 64 bytes) is served
+    // by the LDS 32 lanes at a time over 128 four-byte banks (measured on gfx950: lanes 0-31,
+    // then 32-63); lanes 0-31 read rows 0..15 at two adjacent chunks, and rows r, r + 4, r + 8,
+    // r + 12 share a bank base, so their swizzles must fall in distinct pairs {c, c ^ 1}.
+    static __device__ __forceinline__ int kc_swz(int r) {
+        const int j = (r & 15) >> 1;
+        return (j & 1) | ((j & 2) << 1) | ((j & 4) >> 1);
+    }
     // Chunk swizzle of an MN-contiguous k-row (chunk c of row k sits at c ^ mn_swz(k)).
     static __device__ __forceinline__ int mn_swz(int k) {
         return EB == 2 ? 2 * ((k & 3) ^ ((k >> 3) & 1)) : ((k & 7) ^ ((k >> 4) & 1));
