@@ -95,7 +95,8 @@ def draw(rng: np.random.Generator, shape: tuple, dist: str, fmt: str) -> np.ndar
     """One operand's logical values in storage format.
 
     dist: 'uniform(lo,hi)' continuous, 'normal(mu,sigma)', 'int_uniform(lo,hi)' (inclusive
-    integers), 'zeros', 'ones'."""
+    integers), 'log_uniform(e0,e1)' (random sign, magnitude 2^u with u uniform in [e0, e1):
+    values spread evenly over the binades), 'zeros', 'ones'."""
     name, _, rest = dist.partition("(")
     params = [float(p) for p in rest.rstrip(")").split(",")] if rest else []
     if name == "zeros":
@@ -106,6 +107,8 @@ def draw(rng: np.random.Generator, shape: tuple, dist: str, fmt: str) -> np.ndar
         x = rng.uniform(params[0], params[1], size=shape)
     elif name == "normal":
         x = rng.normal(params[0], params[1], size=shape)
+    elif name == "log_uniform":
+        x = np.exp2(rng.uniform(params[0], params[1], size=shape)) * rng.choice([-1.0, 1.0], size=shape)
     elif name == "int_uniform":
         x = rng.integers(int(params[0]), int(params[1]) + 1, size=shape).astype(np.float64)
     else:

@@ -18,7 +18,8 @@ Pages (cited by title and section):
   * "NVIDIA Tensor Core mixed-precision computing: principles and applications"
     (jsqmd.com/news/1087138) -- section 2.3, rounding model and the error expression
     E = sum(a_i b_i)(1 + d_i) + c(1 + d_c), |d| <= 2^-p, which the bound below instantiates
-    with FP32's p = 23.
+    with FP32's p = 23; sections 2.2-2.3, 3.1 and 4.2.1, the block-FMA model of matrix-core
+    accumulation (``gemm_mfma``), whose open parameters are set to gfx950's measured ones.
 """
 from __future__ import annotations
 
@@ -80,6 +81,15 @@ def _load() -> ctypes.CDLL:
                                              i64, vp, i64, vp]
         lib.oracle_round_array.restype = i32
         lib.oracle_round_array.argtypes = [vp, i64, i32, vp]
+        flt = ctypes.c_float
+        lib.oracle_gemm_mfma_points.restype = i32
+        lib.oracle_gemm_mfma_points.argtypes = [i32, i32, i64, i64, i64, flt, vp, i32, i64, vp,
+                                                i32, i64, flt, vp, i32, i64, i32, i32, i32,
+                                                i32, i64, vp, vp, vp]
+        lib.oracle_gemm_mfma_full.restype = i32
+        lib.oracle_gemm_mfma_full.argtypes = [i32, i32, i64, i64, i64, flt, vp, i32, i64, vp,
+                                              i32, i64, flt, vp, i32, i64, i32, i32, i32, i32,
+                                              vp]
         lib.oracle_num_threads.restype = i32
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -172,6 +182,49 @@ def gemm_fp(transa: bool, transb: bool, m: int, n: int, k: int, alpha: float,
     if rc != 0:
         raise ValueError(f"oracle rejected types a={atype} b={btype} c={ctype} (rc={rc})")
     return FpReference(v, S, bc)
+
+
+# Block-FMA parameters of gfx950's v_mfma_f32_16x16x32_{f16,bf16}: 8 products per block, 24
+# fraction bits below the block's exponent (the 2+23+1 accumulator of the numerics page), and
+# a block sum that keeps 32 significant bits before its rounding to FP32.
+MFMA_BLOCK = 8
+MFMA_FRAC = 24
+MFMA_SUM_BITS = 32
+
+
+def gemm_mfma(transa: bool, transb: bool, m: int, n: int, k: int, alpha: float,
+              A: np.ndarray, atype: str, lda: int, B: np.ndarray, btype: str, ldb: int,
+              beta: float, C: Optional[np.ndarray], ctype: str, ldc: int, out_fmt: str,
+              points: Optional[tuple] = None, nblk: int = MFMA_BLOCK,
+              frac: int = MFMA_FRAC, sum_bits: int = MFMA_SUM_BITS) -> np.ndarray:
+    """Block-FMA model of matrix-core accumulation (mpgemm_oracle.c): the output in
+    ``out_fmt`` storage, bit for bit.  alpha and beta are FP32 values (they are rounded to
+    FP32 here, as the C ABI takes them).  With ``points=(ii, jj)`` only those elements."""
+    _check_storage("A", A, atype)
+    _check_storage("B", B, btype)
+    if beta != 0.0:
+        _check_storage("C", C, ctype)
+    else:
+        C = None
+    lib = _load()
+    args = (int(bool(transa)), int(bool(transb)), m, n, k, float(np.float32(alpha)), _ptr(A),
+            _CODES[atype], lda, _ptr(B), _CODES[btype], ldb, float(np.float32(beta)),
+            _ptr(C), _CODES[ctype], ldc, _CODES[out_fmt], int(nblk), int(frac),
+            int(sum_bits))
+    odt = np.uint32 if out_fmt == "f32" else np.uint16
+    if points is None:
+        D = np.empty((m, n), odt)
+        rc = lib.oracle_gemm_mfma_full(*args, D.ctypes.data)
+    else:
+        ii = np.ascontiguousarray(points[0], dtype=np.int64)
+        jj = np.ascontiguousarray(points[1], dtype=np.int64)
+        D = np.empty(ii.shape, odt)
+        rc = lib.oracle_gemm_mfma_points(*args, ii.size, ii.ctypes.data, jj.ctypes.data,
+                                         D.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"block model rejected a={atype} b={btype} c={ctype} out={out_fmt} "
+                         f"nblk={nblk} frac={frac} sum_bits={sum_bits}")
+    return D.view(np.float32) if out_fmt == "f32" else D
 
 
 def gemm_int(transa: bool, transb: bool, m: int, n: int, k: int, alpha: int,
@@ -302,6 +355,19 @@ def check_fp(D: np.ndarray, out_fmt: str, ref: FpReference, k: int, alpha: float
         detail = (f"first bad flat index {first}: D={Dv[first]!r} v={v[first]!r} "
                   f"ref_rounded={ref_rounded[first]!r}")
     return CheckReport(ok=idx.size == 0, n=n, n_bad=int(idx.size), worst_ratio=worst,
+                       first_bad=first, detail=detail)
+
+
+def check_bits(D: np.ndarray, out_fmt: str, ref: np.ndarray) -> CheckReport:
+    """Bitwise equality of two floating outputs in ``out_fmt`` storage, except that +0 equals
+    -0 and any NaN equals any NaN."""
+    d = output_to_f64(D, out_fmt).reshape(-1)
+    r = output_to_f64(ref, out_fmt).reshape(-1)
+    bad = ~((d == r) | (np.isnan(d) & np.isnan(r)))
+    idx = np.flatnonzero(bad)
+    first = int(idx[0]) if idx.size else None
+    detail = "" if first is None else f"first bad flat index {first}: D={d[first]!r} model={r[first]!r}"
+    return CheckReport(ok=idx.size == 0, n=d.size, n_bad=int(idx.size), worst_ratio=0.0,
                        first_bad=first, detail=detail)
 
 

@@ -115,3 +115,20 @@ def check_case(w: Workload, exact: bool = False, sample: Optional[int] = None, s
     points = None if sample is None else sample_points(w.m, w.n, sample)
     rep = compare(inp, res, exact=exact, points=points)
     return rep, res
+
+
+def model_ref(inp: Inputs, points=None):
+    """The oracle's block-FMA model of the matrix-core accumulation (FP16/BF16 inputs)."""
+    w = inp.w
+    return oracle.gemm_mfma(w.transa, w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda,
+                            inp.B, w.in_type, w.ldb, w.beta, inp.C, w.out_type, w.ldc, w.out_type,
+                            points=points)
+
+
+def compare_model(inp: Inputs, res: GpuResult, points=None):
+    """Bitwise comparison of the GPU output with the block-FMA model (+0 == -0, NaN == NaN)."""
+    w = inp.w
+    D = res.D[:, : w.n]
+    if points is not None:
+        D = D[points[0], points[1]]
+    return oracle.check_bits(np.ascontiguousarray(D), w.out_type, model_ref(inp, points))

@@ -51,3 +51,18 @@ def test_sample_points_in_range():
 def test_named_workloads():
     assert set(WORKLOADS) >= {"f16_256_nn_beta1", "f16_4096_nt", "bf16_8192_nn", "i8_4096_nn",
                               "f16_5000x3000x1000_f16out"}
+
+
+def test_log_uniform_spreads_over_binades():
+    """'log_uniform(e0,e1)': both signs, magnitudes 2^u with u uniform in [e0, e1) (before the
+    one rounding to the storage format), deterministic for a seed."""
+    from gemm_inputs import draw
+    rng = np.random.Generator(np.random.PCG64(3))
+    x = draw(rng, (200, 300), "log_uniform(-20,10)", "f16").view(np.float16).astype(np.float64)
+    e = np.floor(np.log2(np.abs(x[x != 0])))
+    assert e.min() >= -21 and e.max() <= 10
+    counts = np.bincount((e + 21).astype(int), minlength=32)[1:31]
+    assert counts.min() > 0.7 * counts.mean()          # every binade about equally often
+    assert 0.45 < np.mean(x > 0) < 0.55
+    y = draw(np.random.Generator(np.random.PCG64(3)), (200, 300), "log_uniform(-20,10)", "f16")
+    assert np.array_equal(y.view(np.uint16), x.astype(np.float16).view(np.uint16))
