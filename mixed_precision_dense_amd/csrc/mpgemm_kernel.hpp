@@ -373,7 +373,8 @@ __device__ __forceinline__ void drain_mfma(Acc (&acc)[FM][FN]) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Epilogue element: v = alpha * acc + beta * c, converted to the output type.
+// Epilogue element: v = fma(alpha, acc, beta * c) in FP32 (v = alpha * acc when beta == 0, and C
+// is not read), converted to the output type with one round-to-nearest-even.
 // ---------------------------------------------------------------------------------------
 template <int OUT> struct Out;
 template <> struct Out<OUT_F32> {
@@ -391,7 +392,10 @@ template <> struct Out<OUT_F16> {
         return (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
     }
     static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-        // v_cvt_f16_f32: round to nearest even under the default mode
+        // The FP32 value first, then v_cvt_f16_f32 (round to nearest even under the default
+        // mode).  The empty asm keeps the compiler from folding the epilogue's fma and this
+        // conversion into v_fma_mixlo_f16, which rounds the exact result once, to FP16.
+        asm("" : "+v"(v));
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (_Float16)v), r, (int)off, 0, 0);
     }
 };
@@ -645,7 +649,9 @@ void gemm_kernel(Params p) {
                                            (uint32_t)p.beta_i * (uint32_t)cv[r];
                         Out<OUT>::store(rd, out_off(i, j, r), (int)v);
                     } else {
-                        Out<OUT>::store(rd, out_off(i, j, r), p.alpha_f * acc[i][j][r] + p.beta_f * cv[r]);
+                        // one rounding of beta * c, then alpha * acc + (beta * c) fused
+                        Out<OUT>::store(rd, out_off(i, j, r),
+                                        __builtin_fmaf(p.alpha_f, acc[i][j][r], p.beta_f * cv[r]));
                     }
                 }
             }
