@@ -7,6 +7,7 @@ kernel (MFMA bound, measured with HIP events on the launch stream) and the CPU o
 on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+  python bench.py --workload f32_4096_nt_bf16x3   # FP32 GEMM as three BF16 products
   python bench.py --copy-calibration   # a plain copy of known size, for counter scaling
 """
 from __future__ import annotations
@@ -112,6 +113,122 @@ def time_gemm(w, steps: int, warmup: int):
     return wall_ms, kern_ms, tile
 
 
+def time_bf16x3(w, steps: int, warmup: int):
+    """FP32 GEMM from BF16 pieces: returns (wall ms per step, ms per step from HIP events for
+    the whole call (two split kernels and the GEMM), ms per launch of the GEMM kernel alone on
+    the same pieces, tile)."""
+    import torch
+    import mixed_precision_dense_amd as mp
+    from gemm_inputs import generate
+
+    inp = generate(w)
+    dA = mp.device_buffer(inp.A, "f32")
+    dB = mp.device_buffer(inp.B, "f32")
+    dC = mp.device_buffer(inp.C, "f32") if inp.C is not None else None
+    dD = torch.empty(w.m * w.ldc * 4, dtype=torch.uint8, device="cuda")
+    need = mp.mpgemm_bf16x3_workspace_size(w.transa, w.transb, w.m, w.n, w.k)
+    raw = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    ws = (raw.data_ptr() + 255) // 256 * 256
+    stream = torch.cuda.current_stream()
+    h = mp.Handle()
+
+    def step():
+        mp.mpgemm_run_bf16x3(h.h, w.transa, w.transb, w.m, w.n, w.k, w.alpha, dA, w.lda, dB,
+                             w.ldb, w.beta, dC, w.ldc, dD, ws, need, stream=stream)
+
+    def timed(fn, n):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(n):
+            fn()
+        ev1.record(stream)
+        ev1.synchronize()
+        return ev0.elapsed_time(ev1) / n
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    call_ms = timed(step, steps)
+    # the GEMM kernel alone, on the pieces the last call left in the workspace
+    kp = (w.k + 7) // 8 * 8
+    k3 = 3 * kp
+    lda3 = (w.m + 7) // 8 * 8 if w.transa else k3
+    ldb3 = k3 if w.transb else (w.n + 7) // 8 * 8
+    off_b = ((k3 if w.transa else w.m) * lda3 * 2 + 255) // 256 * 256
+
+    def gemm():
+        mp.mpgemm_run(h.h, w.transa, w.transb, w.m, w.n, k3, w.alpha, ws, "bf16", lda3,
+                      ws + off_b, "bf16", ldb3, w.beta, dC, "f32", w.ldc, dD, "f32",
+                      stream=stream)
+
+    gemm_ms = timed(gemm, steps)
+    tile = mp.mpgemm_tile_shape(w.m, w.n, "bf16")
+    h.close()
+    return wall_ms, call_ms, gemm_ms, tile
+
+
+def bf16x3_line(w, args) -> dict:
+    wall_ms, call_ms, gemm_ms, tile = time_bf16x3(w, args.steps, args.warmup)
+    k3 = 3 * ((w.k + 7) // 8 * 8)
+    peak = PEAK_TFLOPS["bf16"]
+    gemm_flops = 2.0 * w.m * w.n * k3            # the GEMM kernel's algorithmic work
+    split_bytes = (4 + 6) * (w.m * w.k + w.k * w.n)   # read FP32, write three BF16 pieces
+    split_ms = call_ms - gemm_ms
+    line = {
+        "metric": "FP32-equivalent TFLOP/s (2mnk per FP32 GEMM) at 1 GPU",
+        "value": round(w.flops / (wall_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "m": w.m, "n": w.n, "k": w.k,
+                   "transa": "T" if w.transa else "N", "transb": "T" if w.transb else "N",
+                   "in": "f32", "products": "3 x bf16 (hi*hi + lo*hi + hi*lo)", "k3": k3,
+                   "accumulate": "f32", "out": "f32", "tile": f"{tile[0]}x{tile[1]}",
+                   "call_ms_events": round(call_ms, 5), "gemm_ms_events": round(gemm_ms, 5),
+                   "split_ms_events": round(split_ms, 5),
+                   "split_hbm_GBs": round(split_bytes / (split_ms * 1e-3) / 1e9, 1),
+                   "fp32_vector_peak_TFLOPs": 157.3},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 2),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_f32(w)
+    return line
+
+
+def cpu_baseline_f32(w, target_s: float = 15.0):
+    """The oracle's double-precision FP32 GEMM on a bounded sample of output elements."""
+    import oracle
+    from gemm_inputs import generate, sample_points
+
+    inp = generate(w)
+    probe = sample_points(w.m, w.n, 2000, seed=99)
+    t0 = time.perf_counter()
+    oracle.gemm_f32(w.transa, w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.lda, inp.B, w.ldb,
+                    w.beta, inp.C, w.ldc, points=probe)
+    per_elem = (time.perf_counter() - t0) / probe[0].size
+    count = min(max(int(target_s / per_elem) - 132, 1), w.m * w.n // 2)
+    pts = sample_points(w.m, w.n, count, seed=99)
+    t0 = time.perf_counter()
+    oracle.gemm_f32(w.transa, w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.lda, inp.B, w.ldb,
+                    w.beta, inp.C, w.ldc, points=pts)
+    t = time.perf_counter() - t0
+    return {"value": 2.0 * pts[0].size * w.k / t / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": (f"{pts[0].size} output elements of the {w.m}x{w.n}x{w.k} workload, each "
+                       f"a {w.k}-term FP32 dot product in double; {t:.1f} s")}
+
+
 def cpu_baseline(w, target_s: float = 15.0):
     """The oracle, as is, on a bounded sample of the workload: whole passes over the full
     output when one pass fits the time budget, else a sample of output elements."""
@@ -175,7 +292,10 @@ def main() -> int:
         copy_calibration()
         return 0
 
-    from gemm_inputs import WORKLOADS
+    from gemm_inputs import NEXT_WORKLOADS, WORKLOADS
+    if args.workload in NEXT_WORKLOADS:
+        print(json.dumps(bf16x3_line(NEXT_WORKLOADS[args.workload], args)), flush=True)
+        return 0
     w = WORKLOADS[args.workload]
     wall_ms, kern_ms, tile = time_gemm(w, args.steps, args.warmup)
     flops = w.flops

@@ -233,6 +233,16 @@ WORKLOADS["f16_5000x3000x1000_f16out_padded"] = Workload(
     note="as above with lda=1008, ldb=ldc=3008")
 
 
+# Workloads of the extensions beyond the five configurations: FP32 operands multiplied as
+# three BF16 products (the same 4096^3 NT shape as the FP16 benchmark workload).
+NEXT_WORKLOADS = {
+    "f32_4096_nt_bf16x3": Workload(
+        "f32_4096_nt_bf16x3", "f32", "f32", 4096, 4096, 4096, transb=True, alpha=1.0, beta=0.0,
+        a_dist="normal(0,1)", b_dist="normal(0,1)", seed=6,
+        note="FP32 4096^3, B stored n x k, as three BF16 products with FP32 accumulation"),
+}
+
+
 def sample_points(m: int, n: int, count: int, seed: int = 12345) -> tuple:
     """Output coordinates for sampled checks: the four corners, the last row and column,
     and ``count`` uniformly drawn points."""

@@ -116,6 +116,49 @@ mpgemm_status_t mpgemm_run(mpgemm_handle_t handle, mpgemm_op_t transa, mpgemm_op
                            const void *beta, const void *C, mpgemm_dtype_t c_type, int64_t ldc,
                            void *D, mpgemm_dtype_t compute_type, void *stream);
 
+/* FP32 GEMM from BF16 pieces (multiword emulation: "NVIDIA Tensor Core mixed-precision
+ * computing: principles and applications", section 5.1, splits high-precision operands into
+ * pieces the matrix cores take and sums the partial products; "The CUDA Handbook" section
+ * 17.5 does FP32 GEMM on Tensor Cores by rounding inputs to TF32).  Queues on `stream`
+ *
+ *   D = alpha * op(A) * op(B) + beta * C        A, B, C, D, alpha, beta: FP32
+ *
+ * with every element x of A and B split into x_hi = RN_bf16(x) and x_lo = RN_bf16(x - x_hi)
+ * (round to nearest even; x - x_hi is exact in FP32; x_lo = 0 when x_hi is Inf or NaN, so
+ * Inf and NaN propagate as in an FP32 product, and finite x beyond BF16's largest value,
+ * about 3.39e38, counts as infinite), and op(A) op(B) replaced by
+ *
+ *   A_hi B_hi + A_lo B_hi + A_hi B_lo
+ *
+ * computed as ONE BF16 GEMM of the kind mpgemm_run performs (FP32 accumulation, same
+ * numerics and epilogue) over k3 = 3 kp, kp = k rounded up to a multiple of 8: the k index
+ * runs through the three products in that order, each zero-padded from k to kp.  Per
+ * element the representation error is at most about 3 * 2^-16 |a b| (A_lo B_lo and the
+ * residuals are dropped), against 2^-11 for inputs rounded to TF32.
+ *
+ *   workspace:       device memory for the split operands, at least
+ *                    mpgemm_bf16x3_workspace_size(transa, transb, m, n, k) bytes, 256-byte
+ *                    aligned, not overlapping A, B, C or D; overwritten, owned by the caller,
+ *                    and in use until the queued work finishes.  Layout (BF16, row-major):
+ *                    A3 at offset 0: m x k3 (ld k3) for transa == N, k3 x m (ld m rounded up
+ *                    to 8) for transa == T; B3 at the next 256-byte boundary: k3 x n (ld n
+ *                    rounded up to 8) for transb == N, n x k3 (ld k3) for transb == T.
+ *   Alignment:       A, B, C (when read), D 16-byte aligned; lda, ldb, ldc multiples of 4.
+ *   Other arguments, ownership and errors as for mpgemm_run; a workspace that is NULL (with
+ *   a nonzero requirement) or smaller than required returns MPGEMM_STATUS_INVALID_VALUE, a
+ *   misaligned one MPGEMM_STATUS_NOT_SUPPORTED.  mpgemm_run_bf16x3 allocates nothing. */
+mpgemm_status_t mpgemm_run_bf16x3(mpgemm_handle_t handle, mpgemm_op_t transa,
+                                  mpgemm_op_t transb, int64_t m, int64_t n, int64_t k,
+                                  const float *alpha, const float *A, int64_t lda,
+                                  const float *B, int64_t ldb, const float *beta,
+                                  const float *C, int64_t ldc, float *D, void *workspace,
+                                  uint64_t workspace_bytes, void *stream);
+
+/* Workspace bytes mpgemm_run_bf16x3 needs for these sizes (0 when m, n or k is 0); 0 also
+ * for negative sizes or flags outside MPGEMM_OP_N / MPGEMM_OP_T.  Host-only. */
+uint64_t mpgemm_bf16x3_workspace_size(mpgemm_op_t transa, mpgemm_op_t transb, int64_t m,
+                                      int64_t n, int64_t k);
+
 /* Host-only argument check: returns exactly the status mpgemm_run would return for these
  * arguments before touching the device (MPGEMM_STATUS_SUCCESS if it would launch).  It needs
  * no handle and no device, and dereferences only alpha and beta. */

@@ -60,6 +60,12 @@ def load() -> ctypes.CDLL:
         lib.mpgemm_status_string.argtypes = [i32]
         lib.mpgemm_tile_shape.restype = i32
         lib.mpgemm_tile_shape.argtypes = [i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        u64 = ctypes.c_uint64
+        lib.mpgemm_run_bf16x3.restype = i32
+        lib.mpgemm_run_bf16x3.argtypes = [vp, i32, i32, i64, i64, i64, vp, vp, i64, vp, i64, vp,
+                                          vp, i64, vp, vp, u64, vp]
+        lib.mpgemm_bf16x3_workspace_size.restype = u64
+        lib.mpgemm_bf16x3_workspace_size.argtypes = [i32, i32, i64, i64, i64]
         _lib = lib
     return _lib
 
@@ -130,6 +136,24 @@ def mpgemm_run(handle, transa, transb, m, n, k, alpha, A, a_type, lda, B, b_type
     if check and st != SUCCESS:
         raise MpgemmError(st, "mpgemm_run")
     return st
+
+
+def mpgemm_run_bf16x3(handle, transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, D,
+                      workspace, workspace_bytes, stream=None, check: bool = True) -> int:
+    """Queue the FP32 GEMM computed from BF16 pieces (three products); FP32 A, B, C, D."""
+    al, be = ctypes.c_float(float(alpha)), ctypes.c_float(float(beta))
+    st = load().mpgemm_run_bf16x3(handle, _op(transa), _op(transb), m, n, k, ctypes.byref(al),
+                                  _ptr(A), lda, _ptr(B), ldb, ctypes.byref(be), _ptr(C), ldc,
+                                  _ptr(D), _ptr(workspace), int(workspace_bytes),
+                                  _stream(stream))
+    if check and st != SUCCESS:
+        raise MpgemmError(st, "mpgemm_run_bf16x3")
+    return st
+
+
+def mpgemm_bf16x3_workspace_size(transa, transb, m: int, n: int, k: int) -> int:
+    """Workspace bytes mpgemm_run_bf16x3 needs (host-only)."""
+    return int(load().mpgemm_bf16x3_workspace_size(_op(transa), _op(transb), m, n, k))
 
 
 def mpgemm_check(transa, transb, m, n, k, alpha, A, a_type, lda, B, b_type, ldb, beta, C,

@@ -72,9 +72,104 @@ bool beta_is_zero(const void *beta, mpgemm_dtype_t compute) {
     return b == 0.0f;  // -0 counts as zero; NaN does not
 }
 
+// Workspace layout of mpgemm_run_bf16x3 (see include/mpgemm.h).
+struct Bf16x3Layout {
+    int64_t k3;            // 3 * (k rounded up to 8)
+    int64_t lda3, ldb3;    // leading dimensions (elements) of the BF16 operands
+    uint64_t off_b;        // byte offset of B3 in the workspace
+    uint64_t total;        // workspace bytes (0 when nothing is split)
+};
+
+bool bf16x3_layout(bool ta, bool tb, int64_t m, int64_t n, int64_t k, Bf16x3Layout &L) {
+    if (m < 0 || n < 0 || k < 0) return false;
+    const int64_t lim = (int64_t)1 << 40;  // keeps every product below 2^63
+    if (m > lim || n > lim || k > lim) return false;
+    L.k3 = 3 * ((k + 7) / 8 * 8);
+    const int64_t m8 = (m + 7) / 8 * 8, n8 = (n + 7) / 8 * 8;
+    // (at least 8: with k == 0 nothing is split, but the BF16 call still checks its strides)
+    L.lda3 = ta ? m8 : (L.k3 > 8 ? L.k3 : 8);
+    L.ldb3 = tb ? (L.k3 > 8 ? L.k3 : 8) : n8;
+    if (m == 0 || n == 0 || k == 0) {
+        L.off_b = L.total = 0;
+        return true;
+    }
+    const unsigned __int128 bytes_a = (unsigned __int128)(ta ? L.k3 : m) * (uint64_t)L.lda3 * 2;
+    const unsigned __int128 bytes_b = (unsigned __int128)(tb ? n : L.k3) * (uint64_t)L.ldb3 * 2;
+    const unsigned __int128 off_b = (bytes_a + 255) / 256 * 256;
+    const unsigned __int128 total = off_b + bytes_b;
+    if (total > (unsigned __int128)UINT64_MAX) return false;
+    L.off_b = (uint64_t)off_b;
+    L.total = (uint64_t)total;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
+
+uint64_t mpgemm_bf16x3_workspace_size(mpgemm_op_t transa, mpgemm_op_t transb, int64_t m,
+                                      int64_t n, int64_t k) {
+    if ((transa != MPGEMM_OP_N && transa != MPGEMM_OP_T) ||
+        (transb != MPGEMM_OP_N && transb != MPGEMM_OP_T))
+        return 0;
+    Bf16x3Layout L;
+    if (!bf16x3_layout(transa == MPGEMM_OP_T, transb == MPGEMM_OP_T, m, n, k, L)) return 0;
+    return L.total;
+}
+
+mpgemm_status_t mpgemm_run_bf16x3(mpgemm_handle_t handle, mpgemm_op_t transa,
+                                  mpgemm_op_t transb, int64_t m, int64_t n, int64_t k,
+                                  const float *alpha, const float *A, int64_t lda,
+                                  const float *B, int64_t ldb, const float *beta,
+                                  const float *C, int64_t ldc, float *D, void *workspace,
+                                  uint64_t workspace_bytes, void *stream) {
+    if (!handle || !handle_live(handle)) return MPGEMM_STATUS_NOT_INITIALIZED;
+    if ((transa != MPGEMM_OP_N && transa != MPGEMM_OP_T) ||
+        (transb != MPGEMM_OP_N && transb != MPGEMM_OP_T))
+        return MPGEMM_STATUS_INVALID_VALUE;
+    if (m < 0 || n < 0 || k < 0 || !alpha || !beta) return MPGEMM_STATUS_INVALID_VALUE;
+    const bool ta = transa == MPGEMM_OP_T, tb = transb == MPGEMM_OP_T;
+    const int64_t min_lda = ta ? m : k, min_ldb = tb ? k : n;
+    if (lda < (min_lda > 1 ? min_lda : 1) || ldb < (min_ldb > 1 ? min_ldb : 1) ||
+        ldc < (n > 1 ? n : 1))
+        return MPGEMM_STATUS_INVALID_VALUE;
+    if (m == 0 || n == 0) return MPGEMM_STATUS_SUCCESS;
+    const bool read_c = !beta_is_zero(beta, MPGEMM_R_32F);
+    if (!D || (k > 0 && (!A || !B)) || (read_c && !C)) return MPGEMM_STATUS_INVALID_VALUE;
+    if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX / 3 - 8) return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (!aligned16(D) || (read_c && !aligned16(C))) return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (k > 0 && (!aligned16(A) || !aligned16(B))) return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (lda % 4 || ldb % 4 || ldc % 4) return MPGEMM_STATUS_NOT_SUPPORTED;
+    Bf16x3Layout L;
+    if (!bf16x3_layout(ta, tb, m, n, k, L)) return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (L.total > 0) {
+        if (!workspace || workspace_bytes < L.total) return MPGEMM_STATUS_INVALID_VALUE;
+        if ((uintptr_t)workspace & 255u) return MPGEMM_STATUS_NOT_SUPPORTED;
+    }
+    char *ws = (char *)workspace;
+    const void *A3 = ws, *B3 = ws ? ws + L.off_b : nullptr;
+    // the GEMM on the pieces must itself be within mpgemm_run's contract (strides, sizes)
+    const mpgemm_status_t st =
+        mpgemm_check(transa, transb, m, n, L.k3, alpha, A3, MPGEMM_R_16BF, L.lda3, B3,
+                     MPGEMM_R_16BF, L.ldb3, beta, C, MPGEMM_R_32F, ldc, D, MPGEMM_R_32F);
+    if (st != MPGEMM_STATUS_SUCCESS) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MPGEMM_STATUS_INTERNAL_ERROR;
+    if (dev != handle->device) return MPGEMM_STATUS_WRONG_DEVICE;
+    hipStream_t s = (hipStream_t)stream;
+    if (k > 0) {
+        // A: pieces (hi, lo, hi); B: pieces (hi, hi, lo)
+        hipError_t e = ta ? mpg::launch_split_bf16x3(A, k, m, lda, ws, L.lda3, false, 0b010, s)
+                          : mpg::launch_split_bf16x3(A, m, k, lda, ws, L.lda3, true, 0b010, s);
+        if (e != hipSuccess) return MPGEMM_STATUS_LAUNCH_FAILED;
+        e = tb ? mpg::launch_split_bf16x3(B, n, k, ldb, ws + L.off_b, L.ldb3, true, 0b100, s)
+               : mpg::launch_split_bf16x3(B, k, n, ldb, ws + L.off_b, L.ldb3, false, 0b100, s);
+        if (e != hipSuccess) return MPGEMM_STATUS_LAUNCH_FAILED;
+    }
+    return mpgemm_run(handle, transa, transb, m, n, L.k3, alpha, A3, MPGEMM_R_16BF, L.lda3, B3,
+                      MPGEMM_R_16BF, L.ldb3, beta, C, MPGEMM_R_32F, ldc, D, MPGEMM_R_32F,
+                      stream);
+}
 
 mpgemm_status_t mpgemm_check(mpgemm_op_t transa, mpgemm_op_t transb, int64_t m, int64_t n,
                              int64_t k, const void *alpha, const void *A, mpgemm_dtype_t a_type,

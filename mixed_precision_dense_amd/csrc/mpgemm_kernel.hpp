@@ -682,5 +682,9 @@ hipError_t launch(const Params &p, hipStream_t stream) {
 hipError_t launch_f16(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
 hipError_t launch_bf16(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
 hipError_t launch_i8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
+// BF16 pieces of an FP32 operand for the three-product GEMM (bf16x3.hip).
+hipError_t launch_split_bf16x3(const float *in, int64_t rows, int64_t cols, int64_t ld_in,
+                               void *out, int64_t ld_out, bool k_along_cols, int pieces,
+                               hipStream_t stream);
 
 }  // namespace mpg

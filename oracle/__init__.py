@@ -90,6 +90,11 @@ def _load() -> ctypes.CDLL:
         lib.oracle_gemm_mfma_full.argtypes = [i32, i32, i64, i64, i64, flt, vp, i32, i64, vp,
                                               i32, i64, flt, vp, i32, i64, i32, i32, i32, i32,
                                               vp]
+        lib.oracle_split_bf16.restype = i32
+        lib.oracle_split_bf16.argtypes = [vp, i64, vp, vp]
+        lib.oracle_gemm_f32_points.restype = i32
+        lib.oracle_gemm_f32_points.argtypes = [i32, i32, i64, dbl, vp, i64, vp, i64, dbl, vp,
+                                               i64, i64, vp, vp, vp, vp]
         lib.oracle_num_threads.restype = i32
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -225,6 +230,111 @@ def gemm_mfma(transa: bool, transb: bool, m: int, n: int, k: int, alpha: float,
         raise ValueError(f"block model rejected a={atype} b={btype} c={ctype} out={out_fmt} "
                          f"nblk={nblk} frac={frac} sum_bits={sum_bits}")
     return D.view(np.float32) if out_fmt == "f32" else D
+
+
+# ----------------------------------------------------------------------------- FP32 via BF16 pieces
+def split_bf16(x: np.ndarray) -> tuple:
+    """x_hi = RN_bf16(x), x_lo = RN_bf16(x - x_hi) (0 where x_hi is not finite), as BF16
+    patterns of x's shape (mpgemm_oracle.c, oracle_split_bf16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    hi = np.empty(x.shape, np.uint16)
+    lo = np.empty(x.shape, np.uint16)
+    _load().oracle_split_bf16(x.ctypes.data, x.size, hi.ctypes.data, lo.ctypes.data)
+    return hi, lo
+
+
+def _rup8(v: int) -> int:
+    return (v + 7) // 8 * 8
+
+
+def bf16x3_operands(transa: bool, transb: bool, m: int, n: int, k: int, A: np.ndarray,
+                    lda: int, B: np.ndarray, ldb: int) -> tuple:
+    """The BF16 operands of the three-product GEMM, built from their definition: k3 = 3 kp
+    (kp = k rounded up to 8); op(A3) = [A_hi | A_lo | A_hi] and op(B3) = [B_hi ; B_hi ; B_lo]
+    along k, each piece zero-padded from k to kp; stored like A and B (transposed when
+    transa / transb), leading dimensions k3 along k and the other size rounded up to 8.
+    Returns (A3, lda3, B3, ldb3, k3)."""
+    kp = _rup8(k)
+    k3 = 3 * kp
+    opA = (A[:k, :m].T if transa else A[:m, :k]).astype(np.float32)     # m x k
+    opB = (B[:n, :k].T if transb else B[:k, :n]).astype(np.float32)     # k x n
+    ah, al = split_bf16(opA)
+    bh, bl = split_bf16(opB)
+    a3 = np.zeros((m, k3), np.uint16)
+    for piece, part in enumerate((ah, al, ah)):
+        a3[:, piece * kp: piece * kp + k] = part
+    b3 = np.zeros((k3, n), np.uint16)
+    for piece, part in enumerate((bh, bh, bl)):
+        b3[piece * kp: piece * kp + k, :] = part
+    if transa:
+        lda3 = _rup8(m)
+        A3 = np.zeros((k3, lda3), np.uint16)
+        A3[:, :m] = a3.T
+    else:
+        lda3 = k3
+        A3 = a3
+    if transb:
+        ldb3 = k3
+        B3 = np.ascontiguousarray(b3.T)
+    else:
+        ldb3 = _rup8(n)
+        B3 = np.zeros((k3, ldb3), np.uint16)
+        B3[:, :n] = b3
+    return np.ascontiguousarray(A3), lda3, np.ascontiguousarray(B3), ldb3, k3
+
+
+def gemm_bf16x3(transa: bool, transb: bool, m: int, n: int, k: int, alpha: float,
+                A: np.ndarray, lda: int, B: np.ndarray, ldb: int, beta: float,
+                C: Optional[np.ndarray], ldc: int, points: Optional[tuple] = None):
+    """The three-product GEMM under the block-FMA model: FP32 output, bit for bit (also the
+    pieces, for the caller's checks).  Returns (D, (A3, lda3, B3, ldb3, k3))."""
+    ops = bf16x3_operands(transa, transb, m, n, k, A, lda, B, ldb)
+    A3, lda3, B3, ldb3, k3 = ops
+    D = gemm_mfma(transa, transb, m, n, k3, alpha, A3, "bf16", lda3, B3, "bf16", ldb3, beta,
+                  C, "f32", ldc, "f32", points=points)
+    return D, ops
+
+
+def gemm_f32(transa: bool, transb: bool, m: int, n: int, k: int, alpha: float,
+             A: np.ndarray, lda: int, B: np.ndarray, ldb: int, beta: float,
+             C: Optional[np.ndarray], ldc: int, points: Optional[tuple] = None) -> tuple:
+    """FP32 GEMM in double (exact products, double sums): (v, S) at the points (default all)."""
+    if points is None:
+        ii, jj = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+        ii, jj = ii.reshape(-1), jj.reshape(-1)
+    else:
+        ii, jj = points
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    B = np.ascontiguousarray(B, dtype=np.float32)
+    Cp = None if beta == 0.0 else np.ascontiguousarray(C, dtype=np.float32)
+    v = np.empty(ii.shape, np.float64)
+    S = np.empty(ii.shape, np.float64)
+    _load().oracle_gemm_f32_points(int(bool(transa)), int(bool(transb)), k, float(alpha),
+                                   A.ctypes.data, lda, B.ctypes.data, ldb, float(beta),
+                                   _ptr(Cp), ldc, ii.size, ii.ctypes.data, jj.ctypes.data,
+                                   v.ctypes.data, S.ctypes.data)
+    if points is None:
+        v, S = v.reshape(m, n), S.reshape(m, n)
+    return v, S
+
+
+# Representation error of the three products per element: |a b - (a_hi b_hi + a_lo b_hi +
+# a_hi b_lo)| <= (3 u^2 + 2 u^3 + ...) |a b| with u = 2^-8 (BF16 unit roundoff).
+BF16X3_PRODUCT_ERROR = 3.0 * 2.0 ** -16 * (1.0 + 2.0 ** -6)
+
+
+def bf16x3_bound(S: np.ndarray, k: int, alpha: float, bc: np.ndarray) -> np.ndarray:
+    """Radius around the double FP32 GEMM within which the three-product result must lie:
+    the products' representation error, FP32 accumulation of 3 kp terms (the section 2.3
+    bound with p = 23, on sums of |pieces| <= (1 + 2^-7) S), one rounding of alpha * acc and
+    of beta * c, and the oracle's own double error."""
+    k3 = 3 * _rup8(k)
+    a = abs(alpha)
+    keff = k3 if _is_pow2_or_zero(alpha) else k3 + 1
+    return (a * S * (BF16X3_PRODUCT_ERROR + keff * 2.0 ** -23 * (1.0 + 2.0 ** -7))
+            + 2.0 ** -23 * np.abs(bc) + a * max(k - 1, 0) * 2.0 ** -53 * S + 1e-300)
 
 
 def gemm_int(transa: bool, transb: bool, m: int, n: int, k: int, alpha: int,

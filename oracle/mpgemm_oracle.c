@@ -638,3 +638,46 @@ int oracle_gemm_mfma_full(int transa, int transb, int64_t m, int64_t n, int64_t 
     free(cols);
     return 0;
 }
+
+/* ======================================================================================
+ * FP32 operands for the three-product BF16 GEMM (multiword emulation).
+ *
+ * "NVIDIA Tensor Core mixed-precision computing: principles and applications", section
+ * 5.1: a high-precision operand is decomposed into pieces the matrix cores take and the
+ * partial products are summed.  An FP32 value x becomes x_hi = RN_bf16(x) and
+ * x_lo = RN_bf16(x - x_hi) (x - x_hi is exact in double), with x_lo = 0 when x_hi is
+ * infinite or NaN.  The GEMM on the pieces is the block model above (or the exact sum).
+ * ====================================================================================== */
+int oracle_split_bf16(const float *x, int64_t count, uint16_t *hi, uint16_t *lo)
+{
+    for (int64_t t = 0; t < count; ++t) {
+        const double v = (double)x[t];
+        const uint64_t h = oracle_encode_rne(v, 8, 7);
+        const double hv = oracle_decode(h, 8, 7);
+        hi[t] = (uint16_t)h;
+        lo[t] = isfinite(hv) ? (uint16_t)oracle_encode_rne(v - hv, 8, 7) : 0;
+    }
+    return 0;
+}
+
+/* Reference FP32 GEMM in double: v = alpha * sum a*b (+ beta * c), S = sum |a*b|, at the
+ * points (ii[t], jj[t]).  An FP32 x FP32 product is exact in double. */
+int oracle_gemm_f32_points(int transa, int transb, int64_t k, double alpha, const float *A,
+                           int64_t lda, const float *B, int64_t ldb, double beta,
+                           const float *C, int64_t ldc, int64_t npts, const int64_t *ii,
+                           const int64_t *jj, double *v, double *S)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < npts; ++t) {
+        double s = 0.0, sa = 0.0;
+        for (int64_t p = 0; p < k; ++p) {
+            const double prod = (double)A[a_index(transa, lda, ii[t], p)] *
+                                (double)B[b_index(transb, ldb, p, jj[t])];
+            s += prod;
+            sa += fabs(prod);
+        }
+        v[t] = beta == 0.0 ? alpha * s : alpha * s + beta * (double)C[ii[t] * ldc + jj[t]];
+        S[t] = sa;
+    }
+    return 0;
+}

@@ -132,3 +132,43 @@ def compare_model(inp: Inputs, res: GpuResult, points=None):
     if points is not None:
         D = D[points[0], points[1]]
     return oracle.check_bits(np.ascontiguousarray(D), w.out_type, model_ref(inp, points))
+
+
+def run_bf16x3(inp: Inputs, in_place: bool = False, workspace_bytes: Optional[int] = None,
+               ws_offset: int = 0, check: bool = True):
+    """Run mpgemm_run_bf16x3 on inp (FP32 A, B, C, D).  Returns (GpuResult, workspace bytes as
+    numpy uint8, status).  D carries GUARD_ROWS sentinel rows; the workspace is a fresh
+    256-byte-aligned allocation (plus ws_offset bytes) filled with 0xA5 before the call."""
+    w = inp.w
+    need = mp.mpgemm_bf16x3_workspace_size(w.transa, w.transb, w.m, w.n, w.k)
+    size = need if workspace_bytes is None else workspace_bytes
+    dA = mp.device_buffer(inp.A, "f32")
+    dB = mp.device_buffer(inp.B, "f32")
+    d_bytes = (w.m + GUARD_ROWS) * w.ldc * 4
+    if in_place:
+        cbuf = np.concatenate([inp.C.view(np.uint8).reshape(-1),
+                               np.full(GUARD_ROWS * w.ldc * 4, SENTINEL, np.uint8)])
+        dC = dD = mp.device_buffer(cbuf, "i8")
+    else:
+        dC = mp.device_buffer(inp.C, "f32") if inp.C is not None else None
+        dD = torch.full((d_bytes,), SENTINEL, dtype=torch.uint8, device="cuda")
+    raw_ws = torch.full((size + 512 + ws_offset,), 0xA5, dtype=torch.uint8, device="cuda")
+    base = raw_ws.data_ptr()
+    ws_ptr = ((base + 255) // 256) * 256 + ws_offset if size else None
+    st = mp.mpgemm_run_bf16x3(handle().h, w.transa, w.transb, w.m, w.n, w.k, w.alpha, dA, w.lda,
+                              dB, w.ldb, w.beta, dC, w.ldc, dD, ws_ptr, size, check=check)
+    torch.cuda.synchronize()
+    raw = dD.cpu().numpy()
+    D = raw[: w.m * w.ldc * 4].view(np.uint8)
+    guard_ok = bool(np.all(raw[w.m * w.ldc * 4:] == SENTINEL))
+    if w.ldc > w.n:
+        pad = D.reshape(w.m, w.ldc * 4)[:, w.n * 4:]
+        if in_place:
+            guard_ok &= bool(np.array_equal(pad, inp.C.view(np.uint8).reshape(w.m, w.ldc * 4)[:, w.n * 4:]))
+        else:
+            guard_ok &= bool(np.all(pad == SENTINEL))
+    ws = raw_ws.cpu().numpy()
+    if ws_ptr is not None:
+        ws = ws[ws_ptr - base: ws_ptr - base + size]
+    res = GpuResult(D=D.view(np.float32).reshape(w.m, w.ldc), guard_ok=guard_ok)
+    return res, ws, st

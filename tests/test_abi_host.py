@@ -145,3 +145,21 @@ def test_tile_shape():
     assert mp.mpgemm_tile_shape(256, 256) == (64, 64)
     assert mp.mpgemm_tile_shape(256, 256, "i8") == (128, 128)
     assert mp.mpgemm_tile_shape(5000, 3000) == (256, 256)
+
+
+def test_bf16x3_workspace_size():
+    ws = mp.mpgemm_bf16x3_workspace_size
+    # 4096^3 NT: A3 = 4096 x 12288 BF16, B3 = 4096 x 12288 BF16, no padding between them
+    assert ws(False, True, 4096, 4096, 4096) == 2 * 4096 * 12288 * 2
+    # transposed storage, ragged: kp = 8, k3 = 24; A3 = 24 x 8 (ld = m rounded up) = 384 B,
+    # B3 at 512: 3 x 24 = 144 B
+    assert ws(True, True, 5, 3, 7) == 512 + 144
+    assert ws(False, False, 5, 3, 7) == 256 + 24 * 8 * 2       # A3 5 x 24 = 240 B -> 256
+    assert ws(False, False, 5, 3, 0) == 0 and ws(False, False, 0, 3, 5) == 0
+    assert ws(False, False, -1, 3, 5) == 0
+    assert mp.load().mpgemm_bf16x3_workspace_size(2, 0, 8, 8, 8) == 0
+
+
+def test_bf16x3_rejects_unknown_handles():
+    assert mp.mpgemm_run_bf16x3(0x1000, False, False, 8, 8, 8, 1.0, P, 8, P, 8, 0.0, None, 8, P,
+                                P, 1 << 20, stream=0, check=False) == ST["NOT_INITIALIZED"]
