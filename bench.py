@@ -8,6 +8,7 @@ on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
   python bench.py --workload f32_4096_nt_bf16x3   # FP32 GEMM as three BF16 products
+  python bench.py --workload e4m3_4096_nt         # FP8 E4M3 inputs
   python bench.py --copy-calibration   # a plain copy of known size, for counter scaling
 """
 from __future__ import annotations
@@ -23,7 +24,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0}   # MI355X dense MFMA
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0, "e4m3": 5000.0,
+               "e5m2": 5000.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "mpgemm_f16_4096_nt_counters.txt")
 
@@ -76,7 +78,7 @@ def time_gemm(w, steps: int, warmup: int):
 
     inp = generate(w)
     dA = mp.device_buffer(inp.A, w.in_type)
-    dB = mp.device_buffer(inp.B, w.in_type)
+    dB = mp.device_buffer(inp.B, w.b_type)
     dC = mp.device_buffer(inp.C, w.out_type) if inp.C is not None else None
     ob = {"f32": 4, "i32": 4, "f16": 2, "bf16": 2}[w.out_type]
     dD = torch.empty(w.m * w.ldc * ob, dtype=torch.uint8, device="cuda")
@@ -88,7 +90,7 @@ def time_gemm(w, steps: int, warmup: int):
 
     def step():
         mp.mpgemm_run(h.h, w.transa, w.transb, w.m, w.n, w.k, alpha, dA, w.in_type, w.lda, dB,
-                      w.in_type, w.ldb, beta, dC, w.out_type, w.ldc, dD, compute, stream=stream)
+                      w.b_type, w.ldb, beta, dC, w.out_type, w.ldc, dD, compute, stream=stream)
 
     for _ in range(warmup):
         step()
@@ -245,6 +247,9 @@ def cpu_baseline(w, target_s: float = 15.0):
         if w.in_type == "i8":
             oracle.gemm_int(w.transa, w.transb, w.m, w.n, w.k, int(w.alpha), inp.A, w.lda, inp.B,
                             w.ldb, int(w.beta), inp.C, w.ldc, points=pts)
+        elif w.in_type in oracle.FP8:
+            oracle.gemm_fp8(w.transa, w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda,
+                            inp.B, w.b_type, w.ldb, w.beta, inp.C, w.out_type, w.ldc, points=pts)
         else:
             oracle.gemm_fp(w.transa, w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda,
                            inp.B, w.in_type, w.ldb, w.beta, inp.C, w.out_type, w.ldc, points=pts)
@@ -293,10 +298,10 @@ def main() -> int:
         return 0
 
     from gemm_inputs import NEXT_WORKLOADS, WORKLOADS
-    if args.workload in NEXT_WORKLOADS:
-        print(json.dumps(bf16x3_line(NEXT_WORKLOADS[args.workload], args)), flush=True)
+    w = WORKLOADS[args.workload] if args.workload in WORKLOADS else NEXT_WORKLOADS[args.workload]
+    if w.in_type == "f32":
+        print(json.dumps(bf16x3_line(w, args)), flush=True)
         return 0
-    w = WORKLOADS[args.workload]
     wall_ms, kern_ms, tile = time_gemm(w, args.steps, args.warmup)
     flops = w.flops
     value = flops / (wall_ms * 1e-3) / 1e12
@@ -319,7 +324,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "m": w.m, "n": w.n, "k": w.k,
                    "transa": "T" if w.transa else "N", "transb": "T" if w.transb else "N",
-                   "in": w.in_type, "accumulate": "i32" if w.in_type == "i8" else "f32",
+                   "in": w.in_type, "in_b": w.b_type,
+                   "accumulate": "i32" if w.in_type == "i8" else "f32",
                    "out": w.out_type, "alpha": w.alpha, "beta": w.beta,
                    "tile": f"{tile[0]}x{tile[1]}", "pct_of_peak": round(100 * value / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,

@@ -19,10 +19,10 @@ from typing import Callable, Optional
 import numpy as np
 
 STORAGE = {"f16": np.uint16, "bf16": np.uint16, "i8": np.int8, "f32": np.float32,
-           "i32": np.int32}
-ELEM_BYTES = {"f16": 2, "bf16": 2, "i8": 1, "f32": 4, "i32": 4}
+           "i32": np.int32, "e4m3": np.uint8, "e5m2": np.uint8}
+ELEM_BYTES = {"f16": 2, "bf16": 2, "i8": 1, "f32": 4, "i32": 4, "e4m3": 1, "e5m2": 1}
 PAD_SENTINEL = {"f16": 0x7E00, "bf16": 0x7FC0, "i8": 0x7F, "f32": np.float32(np.nan),
-                "i32": 0x7F7F7F7F}
+                "i32": 0x7F7F7F7F, "e4m3": 0x7F, "e5m2": 0x7E}    # NaN patterns
 
 
 # ----------------------------------------------------------------------------- rounding
@@ -60,6 +60,42 @@ def f64_to_f32(x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float32)
 
 
+# FP8 formats (OCP): E4M3 has 4 exponent bits (bias 7), 3 fraction bits, no infinities and
+# S.1111.111 as NaN; E5M2 has 5 exponent bits (bias 15), 2 fraction bits, IEEE-style specials.
+_FP8_FIELDS = {"e4m3": (4, 3, 7), "e5m2": (5, 2, 15)}
+
+
+def _fp8_finite_table(fmt: str) -> tuple:
+    """(values, codes) of the non-negative finite patterns of an FP8 format, ascending."""
+    eb, mb, bias = _FP8_FIELDS[fmt]
+    vals, codes = [], []
+    for code in range(128):
+        e, f = code >> mb, code & ((1 << mb) - 1)
+        if fmt == "e5m2" and e == (1 << eb) - 1:
+            continue                                   # Inf / NaN
+        if fmt == "e4m3" and code == 0x7F:
+            continue                                   # NaN
+        v = (f / (1 << mb)) * 2.0 ** (1 - bias) if e == 0 else (1 + f / (1 << mb)) * 2.0 ** (e - bias)
+        vals.append(v)
+        codes.append(code)
+    return np.array(vals), np.array(codes, dtype=np.uint8)
+
+
+def f64_to_fp8_bits(x: np.ndarray, fmt: str) -> np.ndarray:
+    """float64 -> FP8 patterns, rounded once to nearest with ties to the even pattern; beyond
+    the largest finite value the result saturates to it (the draws stay inside the range)."""
+    vals, codes = _fp8_finite_table(fmt)
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    d_hi, d_lo = np.abs(vals[hi] - a), np.abs(a - vals[lo])
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & ((codes[lo] & 1) == 0))
+    c = np.where(pick_lo, codes[lo], codes[hi]).astype(np.uint8)
+    c = np.where(np.signbit(x), c | 0x80, c).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), c).astype(np.uint8)
+
+
 def to_storage(x64: np.ndarray, fmt: str) -> np.ndarray:
     if fmt == "f16":
         return f64_to_f16_bits(x64)
@@ -67,6 +103,8 @@ def to_storage(x64: np.ndarray, fmt: str) -> np.ndarray:
         return f64_to_bf16_bits(x64)
     if fmt == "f32":
         return f64_to_f32(x64)
+    if fmt in _FP8_FIELDS:
+        return f64_to_fp8_bits(x64, fmt)
     raise ValueError(fmt)
 
 
@@ -130,7 +168,7 @@ def padded_ld(cols: int, fmt: str) -> int:
 class Workload:
     """A GEMM problem description plus the recipe of its synthetic inputs."""
     name: str
-    in_type: str            # 'f16' | 'bf16' | 'i8'
+    in_type: str            # 'f16' | 'bf16' | 'i8' | 'f32' | 'e4m3' | 'e5m2' (A's type)
     out_type: str           # 'f32' | 'f16' | 'bf16' | 'i32'
     m: int
     n: int
@@ -147,14 +185,16 @@ class Workload:
     ldc: Optional[int] = None
     seed: int = 0
     note: str = ""
+    b_type: Optional[str] = None   # B's type when it differs from A's (FP8 pairs)
 
     def __post_init__(self):
+        self.b_type = self.in_type if self.b_type is None else self.b_type
         # default leading dimensions: the row length rounded up to a 16-byte multiple (and at
         # least one element), the library's alignment contract
         ra, ca = stored_shape(self.m, self.k, self.transa)
         rb, cb = stored_shape(self.k, self.n, self.transb)
         self.lda = padded_ld(ca, self.in_type) if self.lda is None else self.lda
-        self.ldb = padded_ld(cb, self.in_type) if self.ldb is None else self.ldb
+        self.ldb = padded_ld(cb, self.b_type) if self.ldb is None else self.ldb
         self.ldc = padded_ld(self.n, self.out_type) if self.ldc is None else self.ldc
 
     @property
@@ -164,8 +204,8 @@ class Workload:
     @property
     def compulsory_bytes(self) -> int:
         """Each input read once, D written once, C read once when beta != 0."""
-        es, eo = ELEM_BYTES[self.in_type], ELEM_BYTES[self.out_type]
-        b = self.m * self.k * es + self.k * self.n * es + self.m * self.n * eo
+        es, eb, eo = ELEM_BYTES[self.in_type], ELEM_BYTES[self.b_type], ELEM_BYTES[self.out_type]
+        b = self.m * self.k * es + self.k * self.n * eb + self.m * self.n * eo
         if self.beta != 0:
             b += self.m * self.n * eo
         return b
@@ -193,7 +233,7 @@ def generate(w: Workload, seed: Optional[int] = None, c_when_beta_zero: bool = F
     ra, ca = stored_shape(w.m, w.k, w.transa)
     rb, cb = stored_shape(w.k, w.n, w.transb)
     A = place(draw(rng, (ra, ca), w.a_dist, w.in_type), w.lda, w.in_type)
-    B = place(draw(rng, (rb, cb), w.b_dist, w.in_type), w.ldb, w.in_type)
+    B = place(draw(rng, (rb, cb), w.b_dist, w.b_type), w.ldb, w.b_type)
     C = None
     if w.beta != 0 or c_when_beta_zero:
         C = place(draw(rng, (w.m, w.n), w.c_dist, w.out_type), w.ldc, w.out_type)
@@ -233,13 +273,17 @@ WORKLOADS["f16_5000x3000x1000_f16out_padded"] = Workload(
     note="as above with lda=1008, ldb=ldc=3008")
 
 
-# Workloads of the extensions beyond the five configurations: FP32 operands multiplied as
-# three BF16 products (the same 4096^3 NT shape as the FP16 benchmark workload).
+# Workloads of the extensions beyond the five configurations, on the same 4096^3 NT shape as
+# the FP16 benchmark workload: FP32 operands multiplied as three BF16 products, FP8 inputs.
 NEXT_WORKLOADS = {
     "f32_4096_nt_bf16x3": Workload(
         "f32_4096_nt_bf16x3", "f32", "f32", 4096, 4096, 4096, transb=True, alpha=1.0, beta=0.0,
         a_dist="normal(0,1)", b_dist="normal(0,1)", seed=6,
         note="FP32 4096^3, B stored n x k, as three BF16 products with FP32 accumulation"),
+    "e4m3_4096_nt": Workload(
+        "e4m3_4096_nt", "e4m3", "f32", 4096, 4096, 4096, transb=True, alpha=1.0, beta=0.0,
+        a_dist="normal(0,1)", b_dist="normal(0,1)", seed=8,
+        note="FP8 E4M3 4096^3, B stored n x k, FP32 accumulation and output"),
 }
 
 

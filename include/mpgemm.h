@@ -29,6 +29,9 @@
  *   a_type = b_type = MPGEMM_R_16F,  compute MPGEMM_R_32F, c_type MPGEMM_R_32F or MPGEMM_R_16F
  *   a_type = b_type = MPGEMM_R_16BF, compute MPGEMM_R_32F, c_type MPGEMM_R_32F or MPGEMM_R_16BF
  *   a_type = b_type = MPGEMM_R_8I,   compute MPGEMM_R_32I, c_type MPGEMM_R_32I
+ *   a_type, b_type each MPGEMM_R_8F_E4M3 or MPGEMM_R_8F_E5M2 (either pairing; the two FP8
+ *     formats of "NVIDIA Tensor Core mixed-precision computing: principles and applications",
+ *     section 4.3.1), compute MPGEMM_R_32F, c_type MPGEMM_R_32F or MPGEMM_R_16BF
  * FP16/BF16 outputs are rounded once from the FP32 result, to nearest with ties to even.
  * INT32 accumulation and the epilogue wrap modulo 2^32.
  *
@@ -41,10 +44,15 @@
  * even), starting from zero; the epilogue is alpha * acc when beta == 0, else
  * fma(alpha, acc, beta * c) in FP32.  The result is deterministic: the same inputs give the
  * same bits on every call, tile shape and launch.
+ * FP8 inputs accumulate on gfx950's v_mfma_f32_16x16x128_f8f6f4, whose intermediate sums are
+ * narrower (measured: blocks of 16 products in k order, about 13 fraction bits kept below each
+ * block's largest exponent, each 128-deep partial sum added to the FP32 accumulator with one
+ * rounding); results whose partial sums stay on that grid (small integers, for instance) are
+ * exact, others carry an error up to about 2^-9 of sum |a b| per 128 k.
  *
  * Alignment contract (there is no slower fallback path): A, B, C (when read) and D must be
  * 16-byte aligned, and lda, ldb, ldc times the element size must be multiples of 16 bytes
- * (8 elements for FP16/BF16, 16 for INT8, 4 for FP32/INT32).  m, n and k are arbitrary.
+ * (8 elements for FP16/BF16, 16 for INT8 and FP8, 4 for FP32/INT32).  m, n and k are arbitrary.
  * Operands are read in whole aligned 16-byte blocks: each row of A and B must be readable up
  * to the end of the 16-byte block holding its last element (true of any buffer whose size is
  * rows * ld elements).  Elements beyond the logical row are never used in the result.
@@ -79,7 +87,11 @@ typedef enum {
     MPGEMM_R_16BF = 1,  /* bfloat16: upper 16 bits of an IEEE binary32 */
     MPGEMM_R_8I = 2,    /* signed 8-bit integer */
     MPGEMM_R_32F = 3,   /* IEEE binary32 */
-    MPGEMM_R_32I = 4    /* signed 32-bit integer (two's complement) */
+    MPGEMM_R_32I = 4,   /* signed 32-bit integer (two's complement) */
+    MPGEMM_R_8F_E4M3 = 5, /* FP8 E4M3 (OCP): 1 sign, 4 exponent (bias 7), 3 fraction bits;
+                             no infinities, S.1111.111 is NaN; largest 448, smallest 2^-9 */
+    MPGEMM_R_8F_E5M2 = 6  /* FP8 E5M2 (OCP): 1 sign, 5 exponent (bias 15), 2 fraction bits;
+                             IEEE-style infinities and NaNs; largest 57344, smallest 2^-16 */
 } mpgemm_dtype_t;
 
 typedef enum {

@@ -21,8 +21,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmpgemm.so")
 
 OP_N, OP_T = 0, 1
-R_16F, R_16BF, R_8I, R_32F, R_32I = 0, 1, 2, 3, 4
-DTYPES = {"f16": R_16F, "bf16": R_16BF, "i8": R_8I, "f32": R_32F, "i32": R_32I}
+R_16F, R_16BF, R_8I, R_32F, R_32I, R_8F_E4M3, R_8F_E5M2 = 0, 1, 2, 3, 4, 5, 6
+DTYPES = {"f16": R_16F, "bf16": R_16BF, "i8": R_8I, "f32": R_32F, "i32": R_32I,
+          "e4m3": R_8F_E4M3, "e5m2": R_8F_E5M2}
 STATUS = {0: "SUCCESS", 1: "NOT_INITIALIZED", 2: "INVALID_VALUE", 3: "NOT_SUPPORTED",
           4: "ALLOC_FAILED", 5: "NO_DEVICE", 6: "LAUNCH_FAILED", 7: "INTERNAL_ERROR",
           8: "WRONG_DEVICE"}

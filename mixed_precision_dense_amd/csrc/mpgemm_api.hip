@@ -29,7 +29,9 @@ int elem_bytes(mpgemm_dtype_t t) {
     switch (t) {
     case MPGEMM_R_16F:
     case MPGEMM_R_16BF: return 2;
-    case MPGEMM_R_8I: return 1;
+    case MPGEMM_R_8I:
+    case MPGEMM_R_8F_E4M3:
+    case MPGEMM_R_8F_E5M2: return 1;
     case MPGEMM_R_32F:
     case MPGEMM_R_32I: return 4;
     }
@@ -53,10 +55,29 @@ int out_kind(mpgemm_dtype_t a, mpgemm_dtype_t b, mpgemm_dtype_t c, mpgemm_dtype_
     return -1;
 }
 
-bool valid_dtype(int t) { return t >= MPGEMM_R_16F && t <= MPGEMM_R_32I; }
+bool is_fp8_type(mpgemm_dtype_t t) { return t == MPGEMM_R_8F_E4M3 || t == MPGEMM_R_8F_E5M2; }
 
-// Tile edge: 256 x 256 when that still gives most CUs a tile, else smaller.  INT8 tiles are
-// at least 128 wide (a transposed INT8 operand is staged in 128-column groups).
+// Kernel input kind of an FP8 pair (A format, B format).
+int fp8_kind(mpgemm_dtype_t a, mpgemm_dtype_t b) {
+    const bool a5 = a == MPGEMM_R_8F_E5M2, b5 = b == MPGEMM_R_8F_E5M2;
+    return a5 ? (b5 ? mpg::IN_BF8_BF8 : mpg::IN_BF8_FP8) : (b5 ? mpg::IN_FP8_BF8 : mpg::IN_FP8_FP8);
+}
+
+// Output kind for any supported combination, or -1.
+int kernel_out_kind(mpgemm_dtype_t a, mpgemm_dtype_t b, mpgemm_dtype_t c, mpgemm_dtype_t compute) {
+    if (is_fp8_type(a) && is_fp8_type(b)) {
+        if (compute != MPGEMM_R_32F) return -1;
+        if (c == MPGEMM_R_32F) return mpg::OUT_F32;
+        if (c == MPGEMM_R_16BF) return mpg::OUT_BF16;
+        return -1;
+    }
+    return out_kind(a, b, c, compute);
+}
+
+bool valid_dtype(int t) { return t >= MPGEMM_R_16F && t <= MPGEMM_R_8F_E5M2; }
+
+// Tile edge: 256 x 256 when that still gives most CUs a tile, else smaller.  INT8 and FP8
+// tiles are at least 128 wide (a transposed 1-byte operand is staged in 128-column groups).
 int pick_tile(int64_t m, int64_t n, bool int8) {
     const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
     if (t256 >= 192) return 256;
@@ -104,6 +125,18 @@ bool bf16x3_layout(bool ta, bool tb, int64_t m, int64_t n, int64_t k, Bf16x3Layo
 }
 
 }  // namespace
+
+namespace mpg {
+hipError_t launch_fp8(int in, int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s) {
+    switch (in) {
+    case IN_FP8_FP8: return launch_fp8_fp8(out, ta, tb, tile, p, s);
+    case IN_FP8_BF8: return launch_fp8_bf8(out, ta, tb, tile, p, s);
+    case IN_BF8_FP8: return launch_bf8_fp8(out, ta, tb, tile, p, s);
+    case IN_BF8_BF8: return launch_bf8_bf8(out, ta, tb, tile, p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+}  // namespace mpg
 
 extern "C" {
 
@@ -184,7 +217,7 @@ mpgemm_status_t mpgemm_check(mpgemm_op_t transa, mpgemm_op_t transb, int64_t m, 
     if (!valid_dtype(a_type) || !valid_dtype(b_type) || !valid_dtype(c_type) ||
         !valid_dtype(compute_type))
         return MPGEMM_STATUS_NOT_SUPPORTED;
-    if (out_kind(a_type, b_type, c_type, compute_type) < 0) return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (kernel_out_kind(a_type, b_type, c_type, compute_type) < 0) return MPGEMM_STATUS_NOT_SUPPORTED;
     const bool ta = transa == MPGEMM_OP_T, tb = transb == MPGEMM_OP_T;
     const int64_t min_lda = ta ? m : k, min_ldb = tb ? k : n, min_ldc = n;
     if (lda < (min_lda > 1 ? min_lda : 1) || ldb < (min_ldb > 1 ? min_ldb : 1) ||
@@ -281,10 +314,10 @@ mpgemm_status_t mpgemm_run(mpgemm_handle_t handle, mpgemm_op_t transa, mpgemm_op
         memcpy(&p.alpha_f, alpha, sizeof(float));
         memcpy(&p.beta_f, beta, sizeof(float));
     }
-    const int tile = pick_tile(m, n, a_type == MPGEMM_R_8I);
+    const int tile = pick_tile(m, n, elem_bytes(a_type) == 1);
     p.tiles_m = (int)((m + tile - 1) / tile);
     p.tiles_n = (int)((n + tile - 1) / tile);
-    const int out = out_kind(a_type, b_type, c_type, compute_type);
+    const int out = kernel_out_kind(a_type, b_type, c_type, compute_type);
     const bool ta = transa == MPGEMM_OP_T, tb = transb == MPGEMM_OP_T;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
@@ -292,6 +325,8 @@ mpgemm_status_t mpgemm_run(mpgemm_handle_t handle, mpgemm_op_t transa, mpgemm_op
     case MPGEMM_R_16F: e = mpg::launch_f16(out, ta, tb, tile, p, s); break;
     case MPGEMM_R_16BF: e = mpg::launch_bf16(out, ta, tb, tile, p, s); break;
     case MPGEMM_R_8I: e = mpg::launch_i8(out, ta, tb, tile, p, s); break;
+    case MPGEMM_R_8F_E4M3:
+    case MPGEMM_R_8F_E5M2: e = mpg::launch_fp8(fp8_kind(a_type, b_type), out, ta, tb, tile, p, s); break;
     default: return MPGEMM_STATUS_INTERNAL_ERROR;
     }
     return e == hipSuccess ? MPGEMM_STATUS_SUCCESS : MPGEMM_STATUS_LAUNCH_FAILED;
@@ -315,7 +350,7 @@ const char *mpgemm_status_string(mpgemm_status_t status) {
 mpgemm_status_t mpgemm_tile_shape(int64_t m, int64_t n, mpgemm_dtype_t a_type, int *tile_m,
                                   int *tile_n) {
     if (m < 0 || n < 0 || !tile_m || !tile_n) return MPGEMM_STATUS_INVALID_VALUE;
-    const int t = pick_tile(m, n, a_type == MPGEMM_R_8I);
+    const int t = pick_tile(m, n, elem_bytes(a_type) == 1);
     *tile_m = t;
     *tile_n = t;
     return MPGEMM_STATUS_SUCCESS;

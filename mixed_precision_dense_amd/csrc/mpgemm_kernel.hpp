@@ -60,6 +60,7 @@
 namespace mpg {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -71,7 +72,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 typedef __attribute__((address_space(3))) char lds_char;
 
-enum InKind { IN_F16 = 0, IN_BF16 = 1, IN_I8 = 2 };
+// FP8 kinds name the A and B formats (OCP E4M3 "fp8", E5M2 "bf8").
+enum InKind { IN_F16 = 0, IN_BF16 = 1, IN_I8 = 2, IN_FP8_FP8 = 3, IN_FP8_BF8 = 4, IN_BF8_FP8 = 5,
+              IN_BF8_BF8 = 6 };
+constexpr bool is_fp8(int in) { return in >= IN_FP8_FP8 && in <= IN_BF8_BF8; }
 enum OutKind { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2, OUT_I32 = 3 };
 
 // Kernel arguments (one struct, passed by value).
@@ -359,6 +363,46 @@ template <> struct Mma<IN_I8> {
         asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
     }
 };
+// FP8: one 16 x 16 block over a whole 128-byte stage (128 k).  Operand registers: the two
+// 16-byte fragments of the stage's k steps (low half k step 0, high half k step 1), the same
+// for A and B, so both operands present their k in the same order.  cbsz / blgp select the
+// A / B formats (0 = E4M3, 1 = E5M2).
+template <int IN> struct Mma8;
+template <> struct Mma8<IN_FP8_FP8> {
+    static __device__ __forceinline__ void run(u32x8 a, u32x8 b, f32x4 &c) {
+        asm("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:0 blgp:0" : "+a"(c) : "v"(a), "v"(b));
+    }
+};
+template <> struct Mma8<IN_FP8_BF8> {
+    static __device__ __forceinline__ void run(u32x8 a, u32x8 b, f32x4 &c) {
+        asm("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:0 blgp:1" : "+a"(c) : "v"(a), "v"(b));
+    }
+};
+template <> struct Mma8<IN_BF8_FP8> {
+    static __device__ __forceinline__ void run(u32x8 a, u32x8 b, f32x4 &c) {
+        asm("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:0" : "+a"(c) : "v"(a), "v"(b));
+    }
+};
+template <> struct Mma8<IN_BF8_BF8> {
+    static __device__ __forceinline__ void run(u32x8 a, u32x8 b, f32x4 &c) {
+        asm("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1" : "+a"(c) : "v"(a), "v"(b));
+    }
+};
+template <int IN> struct MmaAcc { typedef typename Mma<IN>::acc_t type; };
+template <> struct MmaAcc<IN_FP8_FP8> { typedef f32x4 type; };
+template <> struct MmaAcc<IN_FP8_BF8> { typedef f32x4 type; };
+template <> struct MmaAcc<IN_BF8_FP8> { typedef f32x4 type; };
+template <> struct MmaAcc<IN_BF8_BF8> { typedef f32x4 type; };
+
+// Half h (0 or 1) of an 8-dword fragment register (element inserts: the compiler writes the
+// loaded registers in place, without copies).
+__device__ __forceinline__ void set_half(u32x8 &v, int h, u32x4 x) {
+    if (h == 0) {
+        v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+    } else {
+        v[4] = x[0]; v[5] = x[1]; v[6] = x[2]; v[7] = x[3];
+    }
+}
 
 // Wait states between the last MFMA of the loop and the first read of its results by any
 // other instruction (more than an 8-pass MFMA's result latency), then every accumulator is
@@ -444,13 +488,14 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 template <int IN, int OUT, bool TA, bool TB, int BM, int BN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(Params p) {
-    constexpr int EB = (IN == IN_I8) ? 1 : 2;
+    constexpr bool kF8 = is_fp8(IN);
+    constexpr int EB = (IN == IN_I8 || kF8) ? 1 : 2;
     constexpr int NSA = BM / 32, NSB = BN / 32;
     constexpr int FM = BM / 32, FN = BN / 32;   // 16-wide MFMA blocks per wave (2 x 2 wave grid)
     constexpr int kStageK = kStageKBytes / EB;
     using OpA = Operand<EB, !TA, NSA>;
     using OpB = Operand<EB, TB, NSB>;
-    using acc_t = typename Mma<IN>::acc_t;
+    using acc_t = typename MmaAcc<IN>::type;
     constexpr int A_BYTES = OpA::kStageBytes, B_BYTES = OpB::kStageBytes;
     constexpr int kLoadsPerStage = OpA::kSlots + OpB::kSlots;   // per wave
 
@@ -518,102 +563,219 @@ void gemm_kernel(Params p) {
         }
     };
 
-    // Fragment registers: two sets, one per k step of a stage.
-    u32x4 fa[2][FM], fb[2][FN];
-    // read unit u (< FM + FN): fragment u of A, or fragment u - FM of B
-    auto read_unit = [&](int set, int parity, int ks, int u) {
-        if (u < FM)
-            fa[set][u] = opa.frag(smem + parity * A_BYTES, wm * FM + u, ks);
-        else
-            fb[set][u - FM] = opb.frag(smem + parity * B_BYTES, wn * FN + (u - FM), ks);
-    };
-    // Loads of one stage: A slots first, then B slots; rs_a / rs_b address the stage.
-    i32x4 rs_a, rs_b;
-    auto load_slot = [&](int parity, int l) {
-        if (l < OpA::kSlots)
-            opa.load(rs_a, lds_w + (uint32_t)(parity * A_BYTES), l);
-        else
-            opb.load(rs_b, lds_w + (uint32_t)(kBuffers * A_BYTES + parity * B_BYTES), l - OpA::kSlots);
-    };
-    // Prepare the resources of stage s (the cursors then move to stage s + 1).
-    auto next_rsrc_a = [&](int s) { rs_a = ca.rsrc(s, nk); ca.advance(); };
-    auto next_rsrc_b = [&](int s) { rs_b = cb.rsrc(s, nk); cb.advance(); };
-    auto no_hook = [&](auto) {};
+    if constexpr (!kF8) {
+        // Fragment registers: two sets, one per k step of a stage.
+        u32x4 fa[2][FM], fb[2][FN];
+        // read unit u (< FM + FN): fragment u of A, or fragment u - FM of B
+        auto read_unit = [&](int set, int parity, int ks, int u) {
+            if (u < FM)
+                fa[set][u] = opa.frag(smem + parity * A_BYTES, wm * FM + u, ks);
+            else
+                fb[set][u - FM] = opb.frag(smem + parity * B_BYTES, wn * FN + (u - FM), ks);
+        };
+        // Loads of one stage: A slots first, then B slots; rs_a / rs_b address the stage.
+        i32x4 rs_a, rs_b;
+        auto load_slot = [&](int parity, int l) {
+            if (l < OpA::kSlots)
+                opa.load(rs_a, lds_w + (uint32_t)(parity * A_BYTES), l);
+            else
+                opb.load(rs_b, lds_w + (uint32_t)(kBuffers * A_BYTES + parity * B_BYTES), l - OpA::kSlots);
+        };
+        // Prepare the resources of stage s (the cursors then move to stage s + 1).
+        auto next_rsrc_a = [&](int s) { rs_a = ca.rsrc(s, nk); ca.advance(); };
+        auto next_rsrc_b = [&](int s) { rs_b = cb.rsrc(s, nk); cb.advance(); };
+        auto no_hook = [&](auto) {};
 
-    // One k step: the FM x FN MFMAs of fragment set `set`, each in its own fenced group with at
-    // most two other instructions -- a wave issues one instruction per four cycles, so more
-    // would hold back the next 16-cycle MFMA.  The fragments of the next k step (into the
-    // other set) are read at the even MFMAs of the first half; the `nl` load slots of the
-    // stage being refilled go to every (kMf / nl)-th MFMA from the second one on.
-    constexpr int kMf = FM * FN, kUnits = FM + FN;
-    auto k_step = [&](auto set_c, int rd_parity, int rd_ks, int ld_parity, auto nl_c, auto &&hook) {
-        constexpr int set = decltype(set_c)::value, nl = decltype(nl_c)::value;
-        // The fragments of this k step were read during the first half of the previous one:
-        // one wait for all of them instead of a wait before each MFMA that uses a new one.
-        wait_lds<0>();
-        static_for<kMf>([&](auto idx_c) {
-            constexpr int idx = decltype(idx_c)::value;
-            constexpr int i = idx / FN, j = idx % FN;
-            Mma<IN>::run(fa[set][i], fb[set][j], acc[i][j]);
-            hook(idx_c);
-            static_for<kUnits>([&](auto u_c) {
-                constexpr int u = decltype(u_c)::value;
-                constexpr int at = 2 * kUnits <= kMf ? 2 * u : (u * kMf) / kUnits;
-                if constexpr (at == idx) read_unit(set ^ 1, rd_parity, rd_ks, u);
+        // One k step: the FM x FN MFMAs of fragment set `set`, each in its own fenced group with at
+        // most two other instructions -- a wave issues one instruction per four cycles, so more
+        // would hold back the next 16-cycle MFMA.  The fragments of the next k step (into the
+        // other set) are read at the even MFMAs of the first half; the `nl` load slots of the
+        // stage being refilled go to every (kMf / nl)-th MFMA from the second one on.
+        constexpr int kMf = FM * FN, kUnits = FM + FN;
+        auto k_step = [&](auto set_c, int rd_parity, int rd_ks, int ld_parity, auto nl_c, auto &&hook) {
+            constexpr int set = decltype(set_c)::value, nl = decltype(nl_c)::value;
+            // The fragments of this k step were read during the first half of the previous one:
+            // one wait for all of them instead of a wait before each MFMA that uses a new one.
+            wait_lds<0>();
+            static_for<kMf>([&](auto idx_c) {
+                constexpr int idx = decltype(idx_c)::value;
+                constexpr int i = idx / FN, j = idx % FN;
+                Mma<IN>::run(fa[set][i], fb[set][j], acc[i][j]);
+                hook(idx_c);
+                static_for<kUnits>([&](auto u_c) {
+                    constexpr int u = decltype(u_c)::value;
+                    constexpr int at = 2 * kUnits <= kMf ? 2 * u : (u * kMf) / kUnits;
+                    if constexpr (at == idx) read_unit(set ^ 1, rd_parity, rd_ks, u);
+                });
+                static_for<nl>([&](auto l_c) {
+                    constexpr int l = decltype(l_c)::value;
+                    constexpr int at = ((l * kMf) / (nl > 0 ? nl : 1) + 1) % kMf;
+                    if constexpr (at == idx) load_slot(ld_parity, l);
+                });
+                __builtin_amdgcn_sched_barrier(0);
             });
-            static_for<nl>([&](auto l_c) {
-                constexpr int l = decltype(l_c)::value;
-                constexpr int at = ((l * kMf) / (nl > 0 ? nl : 1) + 1) % kMf;
-                if constexpr (at == idx) load_slot(ld_parity, l);
+        };
+        using C0 = std::integral_constant<int, 0>;
+        using C1 = std::integral_constant<int, 1>;
+        using CL = std::integral_constant<int, kLoadsPerStage>;
+
+        // Stage s multiplies out of LDS buffers s % 2 in two k steps.  During k step 0 the waves
+        // read the fragments of k step 1.  Then each wave waits (vmcnt) for its loads of stage
+        // s + 1, and one barrier publishes stage s + 1 and certifies that every wave has read its
+        // last fragments of stage s.  During k step 1 the waves read the first fragments of stage
+        // s + 1 and queue the loads of stage s + 2 into the buffers just freed, so every load has
+        // at least one k step to land before the barrier that waits for it.
+        // The resources of stage s + 2 are prepared in odd MFMA groups of k step 0, a few scalar
+        // instructions at a time.
+        auto stage_iter = [&](int s, auto par_c) {
+            constexpr int P = decltype(par_c)::value;
+            k_step(C0{}, P, 1, 0, C0{}, [&](auto idx_c) {
+                constexpr int idx = decltype(idx_c)::value;
+                if constexpr (idx == 1 % kMf) next_rsrc_a(s + 2);
+                if constexpr (idx == 3 % kMf) next_rsrc_b(s + 2);
             });
+            wait_vmem<0>();  // this wave's loads of stage s + 1 have landed
+            fix_stage(s + 1, P ^ 1);
+            __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
-        });
-    };
-    using C0 = std::integral_constant<int, 0>;
-    using C1 = std::integral_constant<int, 1>;
-    using CL = std::integral_constant<int, kLoadsPerStage>;
+            k_step(C1{}, P ^ 1, 0, P, CL{}, no_hook);
+        };
 
-    // Stage s multiplies out of LDS buffers s % 2 in two k steps.  During k step 0 the waves
-    // read the fragments of k step 1.  Then each wave waits (vmcnt) for its loads of stage
-    // s + 1, and one barrier publishes stage s + 1 and certifies that every wave has read its
-    // last fragments of stage s.  During k step 1 the waves read the first fragments of stage
-    // s + 1 and queue the loads of stage s + 2 into the buffers just freed, so every load has
-    // at least one k step to land before the barrier that waits for it.
-    // The resources of stage s + 2 are prepared in odd MFMA groups of k step 0, a few scalar
-    // instructions at a time.
-    auto stage_iter = [&](int s, auto par_c) {
-        constexpr int P = decltype(par_c)::value;
-        k_step(C0{}, P, 1, 0, C0{}, [&](auto idx_c) {
-            constexpr int idx = decltype(idx_c)::value;
-            if constexpr (idx == 1 % kMf) next_rsrc_a(s + 2);
-            if constexpr (idx == 3 % kMf) next_rsrc_b(s + 2);
-        });
-        wait_vmem<0>();  // this wave's loads of stage s + 1 have landed
-        fix_stage(s + 1, P ^ 1);
+        // Prologue: stages 0 and 1 are queued; wait for stage 0.
+        next_rsrc_a(0);
+        next_rsrc_b(0);
+        static_for<kLoadsPerStage>([&](auto l_c) { load_slot(0, decltype(l_c)::value); });
+        next_rsrc_a(1);
+        next_rsrc_b(1);
+        static_for<kLoadsPerStage>([&](auto l_c) { load_slot(1, decltype(l_c)::value); });
+        wait_vmem<kLoadsPerStage>();
+        fix_stage(0, 0);
         __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        k_step(C1{}, P ^ 1, 0, P, CL{}, no_hook);
-    };
+    #pragma unroll
+        for (int u = 0; u < kUnits; ++u) read_unit(0, 0, 0, u);
 
-    // Prologue: stages 0 and 1 are queued; wait for stage 0.
-    next_rsrc_a(0);
-    next_rsrc_b(0);
-    static_for<kLoadsPerStage>([&](auto l_c) { load_slot(0, decltype(l_c)::value); });
-    next_rsrc_a(1);
-    next_rsrc_b(1);
-    static_for<kLoadsPerStage>([&](auto l_c) { load_slot(1, decltype(l_c)::value); });
-    wait_vmem<kLoadsPerStage>();
-    fix_stage(0, 0);
-    __syncthreads();
+        // Stages are taken in pairs (buffer parity 0, then 1).  For an odd number of stages the
+        // last pair's second stage lies past K: its loads read zero records, so it multiplies zeros
+        // into the accumulators, which leaves them unchanged.
+        for (int s = 0; s < nk; s += 2) {
+            stage_iter(s, C0{});
+            stage_iter(s + 1, C1{});
+        }
+
+    } else {
+        // FP8: one v_mfma_f32_16x16x128_f8f6f4 per block and stage, on 8-dword fragments (the
+        // stage's two 64-byte k steps as the two halves).  A stage runs in two halves around
+        // its barrier: half 0 multiplies A blocks 0 .. HM-1, half 1 A blocks HM .. FM-1, each
+        // against every B block, B-block-major.  With one register per fragment, each is
+        // reloaded for the next use as soon as its last MFMA has issued: A blocks HM .. FM-1
+        // of this stage during half 0; after the barrier has published the next stage, A blocks
+        // 0 .. HM-1 at the start of half 1 and B block j right after its last MFMA in half 1.
+        constexpr int HM = FM / 2;
+        constexpr int kHalf = HM * FN;                 // MFMAs per half
+        constexpr int kLastB = (FN - 1) * HM;          // half 0: first MFMA of the last B block
+        constexpr int kReadsBeforeLastB = (2 * HM < (kLastB + 1) / 2) ? 2 * HM : (kLastB + 1) / 2;
+        static_assert(FM % 2 == 0 && FN >= 2, "FP8 tiles");
+        u32x8 fa8[FM], fb8[FN];
+        auto read_a = [&](int parity, int blk, int ks) {
+            set_half(fa8[blk], ks, opa.frag(smem + parity * A_BYTES, wm * FM + blk, ks));
+        };
+        auto read_b = [&](int parity, int blk, int ks) {
+            set_half(fb8[blk], ks, opb.frag(smem + parity * B_BYTES, wn * FN + blk, ks));
+        };
+        i32x4 rs_a, rs_b;
+        auto load_slot = [&](int parity, int l) {
+            if (l < OpA::kSlots)
+                opa.load(rs_a, lds_w + (uint32_t)(parity * A_BYTES), l);
+            else
+                opb.load(rs_b, lds_w + (uint32_t)(kBuffers * A_BYTES + parity * B_BYTES), l - OpA::kSlots);
+        };
+        auto next_rsrc_a = [&](int s) { rs_a = ca.rsrc(s, nk); ca.advance(); };
+        auto next_rsrc_b = [&](int s) { rs_b = cb.rsrc(s, nk); cb.advance(); };
+        using C0 = std::integral_constant<int, 0>;
+        using C1 = std::integral_constant<int, 1>;
+
+        // Half 0 of stage s (buffers P): the last B block's two reads (issued after the last
+        // MFMA of the previous half 1) may still be in flight; they are waited for just before
+        // that block's first MFMA, past the A reads this half has issued by then.
+        auto half0 = [&](int s, auto par_c) {
+            constexpr int P = decltype(par_c)::value;
+            wait_lds<2>();
+            static_for<kHalf>([&](auto t_c) {
+                constexpr int t = decltype(t_c)::value;
+                constexpr int j = t / HM, i = t % HM;
+                if constexpr (t == kLastB && kLastB > 0) wait_lds<kReadsBeforeLastB>();
+                Mma8<IN>::run(fa8[i], fb8[j], acc[i][j]);
+                if constexpr (t == 1 % kHalf) next_rsrc_a(s + 2);
+                if constexpr (t == 3 % kHalf) next_rsrc_b(s + 2);
+                static_for<2 * HM>([&](auto r_c) {     // A blocks HM .. FM-1 of this stage
+                    constexpr int r = decltype(r_c)::value;
+                    if constexpr (2 * r == t) read_a(P, HM + r / 2, r % 2);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        // Half 1 of stage s: the next stage (buffers P ^ 1) is in LDS; the loads of stage s + 2
+        // go to buffers P, which every wave has finished reading.
+        auto half1 = [&](auto par_c) {
+            constexpr int P = decltype(par_c)::value;
+            wait_lds<0>();
+            static_for<kHalf>([&](auto t_c) {
+                constexpr int t = decltype(t_c)::value;
+                constexpr int j = t / HM, i = HM + t % HM;
+                Mma8<IN>::run(fa8[i], fb8[j], acc[i][j]);
+                static_for<2 * HM>([&](auto r_c) {     // next stage: A blocks 0 .. HM-1
+                    constexpr int r = decltype(r_c)::value;
+                    if constexpr (r == t) read_a(P ^ 1, r / 2, r % 2);
+                });
+                static_for<FN>([&](auto jj_c) {        // next stage: B block jj after its last use
+                    constexpr int jj = decltype(jj_c)::value;
+                    if constexpr (t == (jj + 1) * HM - 1) {
+                        read_b(P ^ 1, jj, 0);
+                        read_b(P ^ 1, jj, 1);
+                    }
+                });
+                static_for<kLoadsPerStage>([&](auto l_c) {
+                    constexpr int l = decltype(l_c)::value;
+                    constexpr int at = ((l * kHalf) / kLoadsPerStage + 1) % kHalf;
+                    if constexpr (at == t) load_slot(P, l);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        auto stage8 = [&](int s, auto par_c) {
+            constexpr int P = decltype(par_c)::value;
+            half0(s, par_c);
+            wait_vmem<0>();  // this wave's loads of stage s + 1 have landed
+            fix_stage(s + 1, P ^ 1);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            half1(par_c);
+        };
+
+        // Prologue: stages 0 and 1 queued, stage 0 waited for; then the fragments half 0 of
+        // stage 0 needs first (A blocks 0 .. HM-1, every B block; the last B block last).
+        next_rsrc_a(0);
+        next_rsrc_b(0);
+        static_for<kLoadsPerStage>([&](auto l_c) { load_slot(0, decltype(l_c)::value); });
+        next_rsrc_a(1);
+        next_rsrc_b(1);
+        static_for<kLoadsPerStage>([&](auto l_c) { load_slot(1, decltype(l_c)::value); });
+        wait_vmem<kLoadsPerStage>();
+        fix_stage(0, 0);
+        __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kUnits; ++u) read_unit(0, 0, 0, u);
-
-    // Stages are taken in pairs (buffer parity 0, then 1).  For an odd number of stages the
-    // last pair's second stage lies past K: its loads read zero records, so it multiplies zeros
-    // into the accumulators, which leaves them unchanged.
-    for (int s = 0; s < nk; s += 2) {
-        stage_iter(s, C0{});
-        stage_iter(s + 1, C1{});
+        for (int r = 0; r < 2 * HM; ++r) read_a(0, r / 2, r % 2);
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) {
+            read_b(0, jj, 0);
+            read_b(0, jj, 1);
+        }
+        // once: the loop head then sees at most the last B block's reads of a half 1 pending
+        wait_lds<0>();
+        for (int s = 0; s < nk; s += 2) {
+            stage8(s, C0{});
+            stage8(s + 1, C1{});
+        }
     }
     wait_vmem<0>();  // no direct load into LDS is left in flight when the workgroup ends
     drain_mfma(acc);
@@ -682,6 +844,12 @@ hipError_t launch(const Params &p, hipStream_t stream) {
 hipError_t launch_f16(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
 hipError_t launch_bf16(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
 hipError_t launch_i8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
+hipError_t launch_fp8(int in, int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
+// one FP8 format pair each (kern_fp8_*.hip)
+hipError_t launch_fp8_fp8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
+hipError_t launch_fp8_bf8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
+hipError_t launch_bf8_fp8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
+hipError_t launch_bf8_bf8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
 // BF16 pieces of an FP32 operand for the three-product GEMM (bf16x3.hip).
 hipError_t launch_split_bf16x3(const float *in, int64_t rows, int64_t cols, int64_t ld_in,
                                void *out, int64_t ld_out, bool k_along_cols, int pieces,

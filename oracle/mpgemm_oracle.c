@@ -681,3 +681,104 @@ int oracle_gemm_f32_points(int transa, int transb, int64_t k, double alpha, cons
     }
     return 0;
 }
+
+/* ======================================================================================
+ * FP8 inputs.  "NVIDIA Tensor Core mixed-precision computing: principles and applications",
+ * section 4.3.1, names the two FP8 formats, E4M3 (narrower range, more precision) and E5M2;
+ * their fields are read here as the OCP definitions: E5M2 is IEEE-style (5 exponent bits,
+ * bias 15, 2 fraction bits, infinities and NaNs at exponent 31), E4M3 has 4 exponent bits,
+ * bias 7, 3 fraction bits, no infinities, and only S.1111.111 as NaN (exponent 15 is an
+ * ordinary binade, up to 448).  Products of two FP8 values are exact in double.
+ * ====================================================================================== */
+enum { ORC_E4M3 = 5, ORC_E5M2 = 6 };
+
+double oracle_decode_e4m3(uint32_t bits)
+{
+    const int s = (bits >> 7) & 1, e = (bits >> 3) & 15, f = bits & 7;
+    double mag;
+    if (e == 15 && f == 7)
+        mag = NAN;
+    else if (e == 0)
+        mag = ldexp((double)f, 1 - 7 - 3);
+    else
+        mag = ldexp((double)(f | 8), e - 7 - 3);
+    return s ? -mag : mag;
+}
+
+static double decode8(uint32_t bits, int t)
+{
+    return t == ORC_E4M3 ? oracle_decode_e4m3(bits) : oracle_decode(bits, 5, 2);
+}
+
+static void fp8_point(const double *tab_a, const double *tab_b, int transa, int transb,
+                      int64_t k, double alpha, const uint8_t *A, int64_t lda,
+                      const uint8_t *B, int64_t ldb, double beta, const void *C, int ctype,
+                      int64_t ldc, int64_t i, int64_t j, double *v, double *S, double *bc)
+{
+    double s = 0.0, sa = 0.0;
+    for (int64_t p = 0; p < k; ++p) {
+        const double prod = tab_a[A[a_index(transa, lda, i, p)]] * tab_b[B[b_index(transb, ldb, p, j)]];
+        s += prod;
+        sa += fabs(prod);
+    }
+    double betac = 0.0, out;
+    if (beta == 0.0) {
+        out = alpha * s;
+    } else {
+        betac = beta * c_elem(C, ctype, i * ldc + j);
+        out = alpha * s + betac;
+    }
+    *v = out;
+    *S = sa;
+    *bc = betac;
+}
+
+static int fp8_types_ok(int atype, int btype, int ctype)
+{
+    return (atype == ORC_E4M3 || atype == ORC_E5M2) && (btype == ORC_E4M3 || btype == ORC_E5M2) &&
+           (ctype == ORC_F32 || ctype == ORC_BF16 || ctype == ORC_F16);
+}
+
+/* FP8 GEMM at the points (ii[t], jj[t]): as oracle_gemm_fp_points, for FP8 A and B. */
+int oracle_gemm_fp8_points(int transa, int transb, int64_t m, int64_t n, int64_t k,
+                           double alpha, const void *A, int atype, int64_t lda, const void *B,
+                           int btype, int64_t ldb, double beta, const void *C, int ctype,
+                           int64_t ldc, int64_t npts, const int64_t *ii, const int64_t *jj,
+                           double *v, double *S, double *bc)
+{
+    (void)m; (void)n;
+    if (!fp8_types_ok(atype, btype, ctype))
+        return -1;
+    double tab_a[256], tab_b[256];
+    for (uint32_t b = 0; b < 256; ++b) {
+        tab_a[b] = decode8(b, atype);
+        tab_b[b] = decode8(b, btype);
+    }
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t t = 0; t < npts; ++t)
+        fp8_point(tab_a, tab_b, transa, transb, k, alpha, (const uint8_t *)A, lda,
+                  (const uint8_t *)B, ldb, beta, C, ctype, ldc, ii[t], jj[t], &v[t], &S[t], &bc[t]);
+    return 0;
+}
+
+/* FP8 GEMM over the whole m x n output (row-major v, S, bc with stride n). */
+int oracle_gemm_fp8_full(int transa, int transb, int64_t m, int64_t n, int64_t k,
+                         double alpha, const void *A, int atype, int64_t lda, const void *B,
+                         int btype, int64_t ldb, double beta, const void *C, int ctype,
+                         int64_t ldc, double *v, double *S, double *bc)
+{
+    if (!fp8_types_ok(atype, btype, ctype))
+        return -1;
+    double tab_a[256], tab_b[256];
+    for (uint32_t b = 0; b < 256; ++b) {
+        tab_a[b] = decode8(b, atype);
+        tab_b[b] = decode8(b, btype);
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            fp8_point(tab_a, tab_b, transa, transb, k, alpha, (const uint8_t *)A, lda,
+                      (const uint8_t *)B, ldb, beta, C, ctype, ldc, i, j, &v[i * n + j],
+                      &S[i * n + j], &bc[i * n + j]);
+    return 0;
+}

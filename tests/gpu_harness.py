@@ -43,7 +43,7 @@ def run_gpu(inp: Inputs, d_init: Optional[np.ndarray] = None, in_place: bool = F
     w = inp.w
     ob = ELEM_BYTES[w.out_type]
     dA = mp.device_buffer(inp.A, w.in_type)
-    dB = mp.device_buffer(inp.B, w.in_type)
+    dB = mp.device_buffer(inp.B, w.b_type)
     d_bytes = (w.m + GUARD_ROWS) * w.ldc * ob
     if in_place:
         assert inp.C is not None
@@ -62,7 +62,7 @@ def run_gpu(inp: Inputs, d_init: Optional[np.ndarray] = None, in_place: bool = F
     beta = int(w.beta) if compute == "i32" else w.beta
     for _ in range(repeat):
         mp.mpgemm_run(handle().h, w.transa, w.transb, w.m, w.n, w.k, alpha, dA, w.in_type,
-                      w.lda, dB, w.in_type, w.ldb, beta, dC, w.out_type, w.ldc, dD, compute)
+                      w.lda, dB, w.b_type, w.ldb, beta, dC, w.out_type, w.ldc, dD, compute)
     torch.cuda.synchronize()
     raw = dD.cpu().numpy()
     D = raw[: w.m * w.ldc * ob].view(np.uint8)
@@ -85,6 +85,10 @@ def oracle_ref(inp: Inputs, points=None):
     if w.in_type == "i8":
         return oracle.gemm_int(w.transa, w.transb, w.m, w.n, w.k, int(w.alpha), inp.A, w.lda,
                                inp.B, w.ldb, int(w.beta), inp.C, w.ldc, points=points)
+    if w.in_type in oracle.FP8:
+        return oracle.gemm_fp8(w.transa, w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type,
+                               w.lda, inp.B, w.b_type, w.ldb, w.beta, inp.C, w.out_type, w.ldc,
+                               points=points)
     return oracle.gemm_fp(w.transa, w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda,
                           inp.B, w.in_type, w.ldb, w.beta, inp.C, w.out_type, w.ldc,
                           points=points)
@@ -101,7 +105,7 @@ def compare(inp: Inputs, res: GpuResult, exact: bool = False, points=None,
     if w.in_type == "i8":
         return oracle.check_int(np.ascontiguousarray(D), ref)
     return oracle.check_fp(np.ascontiguousarray(D), w.out_type, ref, w.k, w.alpha, exact=exact,
-                           underflow_floor=underflow_floor)
+                           underflow_floor=underflow_floor, fp8=w.in_type in oracle.FP8)
 
 
 def check_case(w: Workload, exact: bool = False, sample: Optional[int] = None, seed=None,

@@ -28,6 +28,13 @@ returns next to the exact value (in units of 2^-23), and asserts nothing.  Famil
   sumref    ties next to a binade edge, with a last bit of either sign: is that limit set by
             the running value's leading bit or by the sum's, and does the block's product sum
             lose its low bits toward minus infinity or each product toward zero?
+
+FP8 (E5M2 x E5M2, v_mfma_f32_16x16x128_f8f6f4), in the same way:
+  fp8blocks +1 and -1 at k = b, b + 1 beside 2^-30 at k = q: the 2^-30 vanishes when q shares
+            the pair's block, or comes before it in the same 128-deep instruction (the
+            instruction's running sum is cut at the next block's window).
+  fp8window 1 + 2^-x in one block: the block's window width.
+  fp8acc    2^s accumulated over the first 128 k, then 1 + 2^-x: the accumulator's precision.
 """
 import itertools
 import os
@@ -38,7 +45,7 @@ import numpy as np
 
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 
-from gemm_inputs import Workload, generate  # noqa: E402
+from gemm_inputs import Workload, f64_to_fp8_bits, generate  # noqa: E402
 from tests.gpu_harness import run_gpu  # noqa: E402
 
 T12 = 2.0 ** -12
@@ -47,6 +54,12 @@ INF = float("inf")
 
 def storage(x, fmt):
     """Exact bit patterns of values representable in fmt (Inf and NaN included)."""
+    if fmt == "e5m2":
+        import torch
+        bits = f64_to_fp8_bits(x, "e5m2")
+        back = torch.from_numpy(bits).view(torch.float8_e5m2).to(torch.float64).numpy()
+        assert np.all((back == x) | np.isnan(x)), "value not representable in e5m2"
+        return bits
     if fmt == "f16":
         h = x.astype(np.float16)
         ok = np.isnan(x) | (h.astype(np.float64) == x)
@@ -98,6 +111,31 @@ def run(fmt, K, probes):
     inp.B[:K, :T] = storage(b, fmt)
     D = run_gpu(inp).D
     return [float(D[t, t]) for t in range(T)]
+
+
+def fp8_main():
+    print("=== e5m2 x e5m2")
+    K = 256
+    tiny = 2.0 ** -15
+    for b in (0, 16, 32, 112):
+        probes = [[(b, 1.0, 1.0), (b + 1, 1.0, -1.0), (q, tiny, tiny)] for q in range(128) if q not in (b, b + 1)]
+        qs = [q for q in range(128) if q not in (b, b + 1)]
+        res = run("e5m2", K, probes)
+        gone = [q for q, v in zip(qs, res) if v == 0.0]
+        print(f"fp8blocks: pair at k = {b}, {b + 1}: 2^-30 vanished at k in [{min(gone)}, {max(gone)}] "
+              f"({len(gone)} positions)" if gone else f"fp8blocks: pair at {b}: none vanished")
+    probes = [[(0, 1.0, 1.0), (1, 2.0 ** -(x // 2), 2.0 ** -(x - x // 2))] for x in range(10, 20)]
+    res = run("e5m2", K, probes)
+    print("fp8window: 1 + 2^-x, gpu - 1:", [(x, v - 1.0) for x, v in zip(range(10, 20), res)])
+    probes, tags = [], []
+    for sa in (4, 8, 12):
+        for x in (8, 10, 12, 14, 16, 18, 20):
+            probes.append([(0, 2.0 ** (sa // 2), 2.0 ** (sa - sa // 2)), (128, 1.0, 1.0),
+                           (129, 2.0 ** -(x // 2), 2.0 ** -(x - x // 2))])
+            tags.append((sa, x))
+    res = run("e5m2", K, probes)
+    for (sa, x), v in zip(tags, res):
+        print(f"fp8acc: 2^{sa} then 1 + 2^-{x}: gpu - exact = {v - (2.0 ** sa + 1 + 2.0 ** -x):.3g}")
 
 
 def ulp_diff(v, probe):
@@ -195,3 +233,4 @@ def main():
 
 if __name__ == "__main__":
     main()
+    fp8_main()

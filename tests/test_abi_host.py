@@ -163,3 +163,15 @@ def test_bf16x3_workspace_size():
 def test_bf16x3_rejects_unknown_handles():
     assert mp.mpgemm_run_bf16x3(0x1000, False, False, 8, 8, 8, 1.0, P, 8, P, 8, 0.0, None, 8, P,
                                 P, 1 << 20, stream=0, check=False) == ST["NOT_INITIALIZED"]
+
+
+def test_fp8_type_matrix():
+    for a in ("e4m3", "e5m2"):
+        for b in ("e4m3", "e5m2"):
+            assert chk(a_type=a, b_type=b, c_type="f32") == ST["SUCCESS"]
+            assert chk(a_type=a, b_type=b, c_type="bf16") == ST["SUCCESS"]
+            assert chk(a_type=a, b_type=b, c_type="f16") == ST["NOT_SUPPORTED"]
+            assert chk(a_type=a, b_type=b, c_type="f32", compute_type="i32") == ST["NOT_SUPPORTED"]
+    assert chk(a_type="e4m3", b_type="f16") == ST["NOT_SUPPORTED"]
+    assert chk(a_type="e4m3", b_type="e4m3", lda=72) == ST["NOT_SUPPORTED"]     # 16-element rows
+    assert mp.mpgemm_tile_shape(256, 256, "e4m3") == (128, 128)
