@@ -9,6 +9,7 @@ on a bounded sample of the same workload.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
   python bench.py --workload f32_4096_nt_bf16x3   # FP32 GEMM as three BF16 products
   python bench.py --workload e4m3_4096_nt         # FP8 E4M3 inputs
+  python bench.py --workload f16_sp24_4096_nt     # 2:4 structured-sparse FP16 A
   python bench.py --copy-calibration   # a plain copy of known size, for counter scaling
 """
 from __future__ import annotations
@@ -80,6 +81,7 @@ def time_gemm(w, steps: int, warmup: int):
     dA = mp.device_buffer(inp.A, w.in_type)
     dB = mp.device_buffer(inp.B, w.b_type)
     dC = mp.device_buffer(inp.C, w.out_type) if inp.C is not None else None
+    dM = mp.device_buffer(inp.meta, "i8") if w.sparse24 else None
     ob = {"f32": 4, "i32": 4, "f16": 2, "bf16": 2}[w.out_type]
     dD = torch.empty(w.m * w.ldc * ob, dtype=torch.uint8, device="cuda")
     compute = "i32" if w.in_type == "i8" else "f32"
@@ -89,8 +91,14 @@ def time_gemm(w, steps: int, warmup: int):
     h = mp.Handle()
 
     def step():
-        mp.mpgemm_run(h.h, w.transa, w.transb, w.m, w.n, w.k, alpha, dA, w.in_type, w.lda, dB,
-                      w.b_type, w.ldb, beta, dC, w.out_type, w.ldc, dD, compute, stream=stream)
+        if w.sparse24:
+            mp.mpgemm_run_sp24(h.h, w.transb, w.m, w.n, w.k, alpha, dA, w.in_type, w.lda, dM,
+                               w.ld_meta, dB, w.b_type, w.ldb, beta, dC, w.out_type, w.ldc, dD,
+                               stream=stream)
+        else:
+            mp.mpgemm_run(h.h, w.transa, w.transb, w.m, w.n, w.k, alpha, dA, w.in_type, w.lda,
+                          dB, w.b_type, w.ldb, beta, dC, w.out_type, w.ldc, dD, compute,
+                          stream=stream)
 
     for _ in range(warmup):
         step()
@@ -110,7 +118,7 @@ def time_gemm(w, steps: int, warmup: int):
     ev1.record(stream)
     ev1.synchronize()
     kern_ms = ev0.elapsed_time(ev1) / steps
-    tile = mp.mpgemm_tile_shape(w.m, w.n, w.in_type)
+    tile = (256, 128) if w.sparse24 else mp.mpgemm_tile_shape(w.m, w.n, w.in_type)
     h.close()
     return wall_ms, kern_ms, tile
 
@@ -244,7 +252,11 @@ def cpu_baseline(w, target_s: float = 15.0):
 
     def run(pts):
         t0 = time.perf_counter()
-        if w.in_type == "i8":
+        if w.sparse24:
+            oracle.gemm_sp24(w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda, inp.meta,
+                             w.ld_meta, inp.B, w.ldb, w.beta, inp.C, w.out_type, w.ldc,
+                             points=pts)
+        elif w.in_type == "i8":
             oracle.gemm_int(w.transa, w.transb, w.m, w.n, w.k, int(w.alpha), inp.A, w.lda, inp.B,
                             w.ldb, int(w.beta), inp.C, w.ldc, points=pts)
         elif w.in_type in oracle.FP8:
@@ -271,9 +283,12 @@ def cpu_baseline(w, target_s: float = 15.0):
         npts = pts[0].size
         what = (f"{npts} output elements (random points plus the corners, last row and last "
                 f"column) of the {w.m}x{w.n}x{w.k} workload")
-    return {"value": 2.0 * npts * w.k / t / 1e12, "unit": unit,
+    terms = w.k // 2 if w.sparse24 else w.k
+    if w.sparse24:
+        elem += " over the kept values of a 2:4 sparse row"
+    return {"value": 2.0 * npts * terms / t / 1e12, "unit": unit,
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{what}; each element a {w.k}-term {elem}; {t:.1f} s"}
+            "sample": f"{what}; each element a {terms}-term {elem}; {t:.1f} s"}
 
 
 def main() -> int:
@@ -332,6 +347,14 @@ def main() -> int:
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic},
     }
+    if w.sparse24:
+        # the work is the kept products (2 m n k/2); the dense GEMM of the same shape would be
+        # twice that
+        line["metric"] = ("TFLOP/s of the kept products (2 m n k/2) of a 2:4 sparse A, and % "
+                          "of MI355X dense MFMA peak at 1 GPU")
+        line["config"]["sparsity"] = "2:4 on A (kept values m x k/2 plus 2-bit positions)"
+        line["config"]["dense_equivalent_TFLOPs"] = round(2 * value, 2)
+        line["config"]["transa"] = "N"
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     if args.all:

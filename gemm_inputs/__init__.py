@@ -186,9 +186,14 @@ class Workload:
     seed: int = 0
     note: str = ""
     b_type: Optional[str] = None   # B's type when it differs from A's (FP8 pairs)
+    sparse24: bool = False         # A 2:4 structured-sparse: A holds the kept values (m x k/2)
+    ld_meta: Optional[int] = None  # bytes per row of the 2:4 metadata
 
     def __post_init__(self):
         self.b_type = self.in_type if self.b_type is None else self.b_type
+        if self.sparse24:
+            self.lda = padded_ld(self.k // 2, self.in_type) if self.lda is None else self.lda
+            self.ld_meta = ((max(self.k // 8, 1) + 15) // 16) * 16 if self.ld_meta is None else self.ld_meta
         # default leading dimensions: the row length rounded up to a 16-byte multiple (and at
         # least one element), the library's alignment contract
         ra, ca = stored_shape(self.m, self.k, self.transa)
@@ -199,13 +204,17 @@ class Workload:
 
     @property
     def flops(self) -> int:
-        return 2 * self.m * self.n * self.k
+        """Multiply-adds the product needs, two flops each (a 2:4 sparse A: the kept ones)."""
+        return 2 * self.m * self.n * (self.k // 2 if self.sparse24 else self.k)
 
     @property
     def compulsory_bytes(self) -> int:
-        """Each input read once, D written once, C read once when beta != 0."""
+        """Each input read once, D written once, C read once when beta != 0 (a 2:4 sparse A:
+        its kept values and metadata)."""
         es, eb, eo = ELEM_BYTES[self.in_type], ELEM_BYTES[self.b_type], ELEM_BYTES[self.out_type]
-        b = self.m * self.k * es + self.k * self.n * eb + self.m * self.n * eo
+        a = (self.m * (self.k // 2) * es + self.m * (self.k // 8) if self.sparse24
+             else self.m * self.k * es)
+        b = a + self.k * self.n * eb + self.m * self.n * eo
         if self.beta != 0:
             b += self.m * self.n * eo
         return b
@@ -217,6 +226,7 @@ class Inputs:
     A: np.ndarray
     B: np.ndarray
     C: Optional[np.ndarray]   # stored m x ldc in out_type, or None when beta == 0
+    meta: Optional[np.ndarray] = None   # 2:4 metadata, m x ld_meta bytes (sparse A only)
 
     @property
     def transa(self):
@@ -230,6 +240,8 @@ class Inputs:
 def generate(w: Workload, seed: Optional[int] = None, c_when_beta_zero: bool = False) -> Inputs:
     """Draw A, then B, then C for ``w`` with PCG64(seed) (default: w.seed)."""
     rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    if w.sparse24:
+        return _generate_sp24(w, rng, c_when_beta_zero)
     ra, ca = stored_shape(w.m, w.k, w.transa)
     rb, cb = stored_shape(w.k, w.n, w.transb)
     A = place(draw(rng, (ra, ca), w.a_dist, w.in_type), w.lda, w.in_type)
@@ -280,11 +292,44 @@ NEXT_WORKLOADS = {
         "f32_4096_nt_bf16x3", "f32", "f32", 4096, 4096, 4096, transb=True, alpha=1.0, beta=0.0,
         a_dist="normal(0,1)", b_dist="normal(0,1)", seed=6,
         note="FP32 4096^3, B stored n x k, as three BF16 products with FP32 accumulation"),
+    "f16_sp24_4096_nt": Workload(
+        "f16_sp24_4096_nt", "f16", "f32", 4096, 4096, 4096, transb=True, alpha=1.0, beta=0.0,
+        a_dist="normal(0,1)", b_dist="normal(0,1)", seed=10, sparse24=True,
+        note="FP16 4096^3 with a 2:4 sparse A (kept values 4096 x 2048), B stored n x k"),
     "e4m3_4096_nt": Workload(
         "e4m3_4096_nt", "e4m3", "f32", 4096, 4096, 4096, transb=True, alpha=1.0, beta=0.0,
         a_dist="normal(0,1)", b_dist="normal(0,1)", seed=8,
         note="FP8 E4M3 4096^3, B stored n x k, FP32 accumulation and output"),
 }
+
+
+# The six ways to keep two of four positions, in increasing order.
+SP24_PAIRS = ((0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3))
+
+
+def pack_sp24_meta(idx: np.ndarray, ld_meta: int) -> np.ndarray:
+    """2-bit indices (m x k/2, values 0..3, in k order) -> m x ld_meta metadata bytes: index j
+    of a row in bits 2 (j % 4) .. +1 of byte j / 4; padding bytes 0xFF."""
+    m, kh = idx.shape
+    meta = np.full((m, ld_meta), 0xFF, np.uint8)
+    q = idx.astype(np.uint8).reshape(m, kh // 4, 4)
+    meta[:, : kh // 4] = q[..., 0] | (q[..., 1] << 2) | (q[..., 2] << 4) | (q[..., 3] << 6)
+    return meta
+
+
+def _generate_sp24(w: "Workload", rng, c_when_beta_zero: bool) -> "Inputs":
+    """A 2:4 sparse A: per group of 4 consecutive k one of the six position pairs (uniform),
+    then the kept values from a_dist (m x k/2), then B and C as usual."""
+    assert not w.transa and w.k % 4 == 0
+    pairs = np.array(SP24_PAIRS, dtype=np.uint8)[rng.integers(0, 6, size=(w.m, w.k // 4))]
+    idx = pairs.reshape(w.m, w.k // 2)
+    A = place(draw(rng, (w.m, w.k // 2), w.a_dist, w.in_type), w.lda, w.in_type)
+    rb, cb = stored_shape(w.k, w.n, w.transb)
+    B = place(draw(rng, (rb, cb), w.b_dist, w.b_type), w.ldb, w.b_type)
+    C = None
+    if w.beta != 0 or c_when_beta_zero:
+        C = place(draw(rng, (w.m, w.n), w.c_dist, w.out_type), w.ldc, w.out_type)
+    return Inputs(w, A, B, C, meta=pack_sp24_meta(idx, w.ld_meta))
 
 
 def sample_points(m: int, n: int, count: int, seed: int = 12345) -> tuple:

@@ -166,6 +166,44 @@ mpgemm_status_t mpgemm_run_bf16x3(mpgemm_handle_t handle, mpgemm_op_t transa,
                                   const float *C, int64_t ldc, float *D, void *workspace,
                                   uint64_t workspace_bytes, void *stream);
 
+/* GEMM with a 2:4 structured-sparse A (the page "稀疏张量核心加速模板计算的技术解析" on sparse tensor
+ * cores for stencils, sections
+ * 1.2.1 and 1.3.2: at most two nonzeros in every group of 4 consecutive k, stored as the kept
+ * values plus 2 bits of metadata per kept value; here on gfx950's v_smfmac sparse matrix
+ * cores).  Queues on `stream`
+ *
+ *   D = alpha * A * op(B) + beta * C,   A(i, 4q + idx(i, j)) += Ac(i, j) for j = 2q, 2q + 1
+ *
+ * i.e. D(i, c) = alpha * sum_j Ac(i, j) * op(B)(4 (j / 2) + idx(i, j), c) + beta * C(i, c).
+ *   Ac:     the kept values, m x k/2, row-major: Ac(i, j) at Ac[i*lda + j], lda >= k/2.
+ *   meta:   m rows of ld_meta bytes, ld_meta >= k/8: idx(i, j) is bits 2 (j % 4) .. +1 of byte
+ *           meta[i*ld_meta + j/4] (2 bits per kept value, in k order, little-endian).  The two
+ *           indices of a group are normally distinct; equal ones make both values multiply
+ *           the same row of op(B).
+ *   B, C, D, transb, ldb, ldc, alpha, beta: as for mpgemm_run; A is never transposed.
+ *   Types:  a_type = b_type = MPGEMM_R_16F or MPGEMM_R_16BF, compute MPGEMM_R_32F, c_type
+ *           MPGEMM_R_32F or a_type.  Numerics as for the dense FP16/BF16 GEMM, over the k/2
+ *           kept products.
+ *   Sizes:  k a multiple of 128 (else MPGEMM_STATUS_NOT_SUPPORTED); m, n arbitrary.
+ *   Alignment: Ac, meta, B, C (when read), D 16-byte aligned; lda and ldb multiples of 8,
+ *           ld_meta of 16 bytes, ldc as for mpgemm_run.
+ * Ownership, ordering and errors as for mpgemm_run; nothing is allocated. */
+mpgemm_status_t mpgemm_run_sp24(mpgemm_handle_t handle, mpgemm_op_t transb, int64_t m, int64_t n,
+                                int64_t k, const void *alpha, const void *Ac,
+                                mpgemm_dtype_t a_type, int64_t lda, const void *meta,
+                                int64_t ld_meta, const void *B, mpgemm_dtype_t b_type,
+                                int64_t ldb, const void *beta, const void *C,
+                                mpgemm_dtype_t c_type, int64_t ldc, void *D,
+                                mpgemm_dtype_t compute_type, void *stream);
+
+/* Host-only argument check of mpgemm_run_sp24 (as mpgemm_check is for mpgemm_run). */
+mpgemm_status_t mpgemm_check_sp24(mpgemm_op_t transb, int64_t m, int64_t n, int64_t k,
+                                  const void *alpha, const void *Ac, mpgemm_dtype_t a_type,
+                                  int64_t lda, const void *meta, int64_t ld_meta, const void *B,
+                                  mpgemm_dtype_t b_type, int64_t ldb, const void *beta,
+                                  const void *C, mpgemm_dtype_t c_type, int64_t ldc,
+                                  const void *D, mpgemm_dtype_t compute_type);
+
 /* Workspace bytes mpgemm_run_bf16x3 needs for these sizes (0 when m, n or k is 0); 0 also
  * for negative sizes or flags outside MPGEMM_OP_N / MPGEMM_OP_T.  Host-only. */
 uint64_t mpgemm_bf16x3_workspace_size(mpgemm_op_t transa, mpgemm_op_t transb, int64_t m,

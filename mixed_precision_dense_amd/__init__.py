@@ -61,6 +61,12 @@ def load() -> ctypes.CDLL:
         lib.mpgemm_status_string.argtypes = [i32]
         lib.mpgemm_tile_shape.restype = i32
         lib.mpgemm_tile_shape.argtypes = [i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        lib.mpgemm_run_sp24.restype = i32
+        lib.mpgemm_run_sp24.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, i64, vp, i64, vp, i32,
+                                        i64, vp, vp, i32, i64, vp, i32, vp]
+        lib.mpgemm_check_sp24.restype = i32
+        lib.mpgemm_check_sp24.argtypes = [i32, i64, i64, i64, vp, vp, i32, i64, vp, i64, vp, i32,
+                                          i64, vp, vp, i32, i64, vp, i32]
         u64 = ctypes.c_uint64
         lib.mpgemm_run_bf16x3.restype = i32
         lib.mpgemm_run_bf16x3.argtypes = [vp, i32, i32, i64, i64, i64, vp, vp, i64, vp, i64, vp,
@@ -150,6 +156,30 @@ def mpgemm_run_bf16x3(handle, transa, transb, m, n, k, alpha, A, lda, B, ldb, be
     if check and st != SUCCESS:
         raise MpgemmError(st, "mpgemm_run_bf16x3")
     return st
+
+
+def mpgemm_run_sp24(handle, transb, m, n, k, alpha, Ac, a_type, lda, meta, ld_meta, B, b_type,
+                    ldb, beta, C, c_type, ldc, D, compute_type="f32", stream=None,
+                    check: bool = True) -> int:
+    """Queue the GEMM with a 2:4 structured-sparse A given as kept values Ac and metadata."""
+    al, be = ctypes.c_float(float(alpha)), ctypes.c_float(float(beta))
+    st = load().mpgemm_run_sp24(handle, _op(transb), m, n, k, ctypes.byref(al), _ptr(Ac),
+                                _dtype(a_type), lda, _ptr(meta), ld_meta, _ptr(B), _dtype(b_type),
+                                ldb, ctypes.byref(be), _ptr(C), _dtype(c_type), ldc, _ptr(D),
+                                _dtype(compute_type), _stream(stream))
+    if check and st != SUCCESS:
+        raise MpgemmError(st, "mpgemm_run_sp24")
+    return st
+
+
+def mpgemm_check_sp24(transb, m, n, k, alpha, Ac, a_type, lda, meta, ld_meta, B, b_type, ldb,
+                      beta, C, c_type, ldc, D, compute_type="f32") -> int:
+    """Host-only argument check of mpgemm_run_sp24."""
+    al, be = ctypes.c_float(float(alpha)), ctypes.c_float(float(beta))
+    return load().mpgemm_check_sp24(_op(transb), m, n, k, ctypes.byref(al), _ptr(Ac),
+                                    _dtype(a_type), lda, _ptr(meta), ld_meta, _ptr(B),
+                                    _dtype(b_type), ldb, ctypes.byref(be), _ptr(C), _dtype(c_type),
+                                    ldc, _ptr(D), _dtype(compute_type))
 
 
 def mpgemm_bf16x3_workspace_size(transa, transb, m: int, n: int, k: int) -> int:

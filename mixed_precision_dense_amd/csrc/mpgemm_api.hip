@@ -332,6 +332,85 @@ mpgemm_status_t mpgemm_run(mpgemm_handle_t handle, mpgemm_op_t transa, mpgemm_op
     return e == hipSuccess ? MPGEMM_STATUS_SUCCESS : MPGEMM_STATUS_LAUNCH_FAILED;
 }
 
+mpgemm_status_t mpgemm_check_sp24(mpgemm_op_t transb, int64_t m, int64_t n, int64_t k,
+                                  const void *alpha, const void *Ac, mpgemm_dtype_t a_type,
+                                  int64_t lda, const void *meta, int64_t ld_meta, const void *B,
+                                  mpgemm_dtype_t b_type, int64_t ldb, const void *beta,
+                                  const void *C, mpgemm_dtype_t c_type, int64_t ldc,
+                                  const void *D, mpgemm_dtype_t compute_type) {
+    if (transb != MPGEMM_OP_N && transb != MPGEMM_OP_T) return MPGEMM_STATUS_INVALID_VALUE;
+    if (m < 0 || n < 0 || k < 0 || !alpha || !beta) return MPGEMM_STATUS_INVALID_VALUE;
+    if (!valid_dtype(a_type) || !valid_dtype(b_type) || !valid_dtype(c_type) ||
+        !valid_dtype(compute_type))
+        return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (a_type != b_type || (a_type != MPGEMM_R_16F && a_type != MPGEMM_R_16BF) ||
+        compute_type != MPGEMM_R_32F || (c_type != MPGEMM_R_32F && c_type != a_type))
+        return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (k % 128) return MPGEMM_STATUS_NOT_SUPPORTED;
+    const bool tb = transb == MPGEMM_OP_T;
+    const int64_t min_ldb = tb ? k : n;
+    if (lda < (k / 2 > 1 ? k / 2 : 1) || ld_meta < (k / 8 > 1 ? k / 8 : 1) ||
+        ldb < (min_ldb > 1 ? min_ldb : 1) || ldc < (n > 1 ? n : 1))
+        return MPGEMM_STATUS_INVALID_VALUE;
+    if (m == 0 || n == 0) return MPGEMM_STATUS_SUCCESS;
+    const bool read_c = !beta_is_zero(beta, compute_type);
+    if (!D || (k > 0 && (!Ac || !meta || !B)) || (read_c && !C)) return MPGEMM_STATUS_INVALID_VALUE;
+    if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return MPGEMM_STATUS_NOT_SUPPORTED;
+    const int ec = elem_bytes(c_type);
+    if (!aligned16(D) || (read_c && !aligned16(C))) return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (k > 0 && (!aligned16(Ac) || !aligned16(meta) || !aligned16(B))) return MPGEMM_STATUS_NOT_SUPPORTED;
+    if ((lda * 2) % 16 || (ldb * 2) % 16 || ld_meta % 16 || (ldc * ec) % 16)
+        return MPGEMM_STATUS_NOT_SUPPORTED;
+    const int64_t limit = ((int64_t)1 << 31) - 4096;
+    if (256 * lda * 2 > limit || 256 * ldb * 2 > limit || 256 * ld_meta > limit ||
+        256 * ldc * ec > limit)
+        return MPGEMM_STATUS_NOT_SUPPORTED;
+    return MPGEMM_STATUS_SUCCESS;
+}
+
+mpgemm_status_t mpgemm_run_sp24(mpgemm_handle_t handle, mpgemm_op_t transb, int64_t m, int64_t n,
+                                int64_t k, const void *alpha, const void *Ac,
+                                mpgemm_dtype_t a_type, int64_t lda, const void *meta,
+                                int64_t ld_meta, const void *B, mpgemm_dtype_t b_type,
+                                int64_t ldb, const void *beta, const void *C,
+                                mpgemm_dtype_t c_type, int64_t ldc, void *D,
+                                mpgemm_dtype_t compute_type, void *stream) {
+    if (!handle || !handle_live(handle)) return MPGEMM_STATUS_NOT_INITIALIZED;
+    const mpgemm_status_t st =
+        mpgemm_check_sp24(transb, m, n, k, alpha, Ac, a_type, lda, meta, ld_meta, B, b_type, ldb,
+                          beta, C, c_type, ldc, D, compute_type);
+    if (st != MPGEMM_STATUS_SUCCESS) return st;
+    if (m == 0 || n == 0) return MPGEMM_STATUS_SUCCESS;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MPGEMM_STATUS_INTERNAL_ERROR;
+    if (dev != handle->device) return MPGEMM_STATUS_WRONG_DEVICE;
+    mpg::SpParams sp;
+    mpg::Params &p = sp.p;
+    p.A = Ac;
+    p.B = B;
+    p.D = D;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.m = (int)m;
+    p.n = (int)n;
+    p.k = (int)k;
+    p.read_c = beta_is_zero(beta, compute_type) ? 0 : 1;
+    p.C = p.read_c ? C : nullptr;
+    memcpy(&p.alpha_f, alpha, sizeof(float));
+    memcpy(&p.beta_f, beta, sizeof(float));
+    p.alpha_i = p.beta_i = 0;
+    p.tiles_m = (int)((m + mpg::kSpTileM - 1) / mpg::kSpTileM);
+    p.tiles_n = (int)((n + mpg::kSpTileN - 1) / mpg::kSpTileN);
+    sp.meta = meta;
+    sp.ld_meta = ld_meta;
+    const int in = a_type == MPGEMM_R_16F ? mpg::IN_F16 : mpg::IN_BF16;
+    const int out = c_type == MPGEMM_R_32F ? mpg::OUT_F32
+                                          : (a_type == MPGEMM_R_16F ? mpg::OUT_F16 : mpg::OUT_BF16);
+    const hipError_t e = mpg::launch_sp24(in, out, transb == MPGEMM_OP_T, sp, (hipStream_t)stream);
+    return e == hipSuccess ? MPGEMM_STATUS_SUCCESS : MPGEMM_STATUS_LAUNCH_FAILED;
+}
+
 const char *mpgemm_status_string(mpgemm_status_t status) {
     switch (status) {
     case MPGEMM_STATUS_SUCCESS: return "success";

@@ -483,6 +483,66 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 }
 
 // ---------------------------------------------------------------------------------------
+// Epilogue of one tile: D = alpha * acc + beta * C, masked to m x n.  kInt: INT32 wrap-around
+// arithmetic (INT8 inputs), else FP32 (see Out<>).  The 2 x 2 waves each hold FM x FN 16 x 16
+// blocks of a BM x BN tile.
+// ---------------------------------------------------------------------------------------
+template <bool kInt, int OUT, int FM, int FN, int BM, int BN, typename AccT>
+__device__ __forceinline__ void store_tile(const Params &p, AccT (&acc)[FM][FN], int m0, int n0,
+                                           int wm, int wn, int lane, bool full_mn, int m_left,
+                                           int n_left) {
+    constexpr int OB = Out<OUT>::kBytes;
+    const int64_t tile_off = ((int64_t)m0 * p.ldc + n0) * OB;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.D + tile_off);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const char *)(p.read_c ? p.C : p.D) + tile_off);
+    const uint32_t ldc_b = (uint32_t)(p.ldc * OB);
+    // accumulator register r of block (i, j): row 16 i + 4 (lane / 16) + r, column 16 j + lane % 16
+    const int row_base = wm * (BM / 2) + 4 * (lane / 16);
+    const int col_base = wn * (BN / 2) + (lane % 16);
+    // byte offset of accumulator element r of block (i, j), or an out-of-range offset
+    auto out_off = [&](int i, int j, int r) -> uint32_t {
+        const int row = row_base + i * 16 + r;
+        const int col = col_base + j * 16;
+        const bool ok = full_mn || (row < m_left && col < n_left);
+        return ok ? (uint32_t)row * ldc_b + (uint32_t)col * OB : kOobOffset;
+    };
+    if (p.read_c) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                decltype(Out<OUT>::load(rc, 0)) cv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) cv[r] = Out<OUT>::load(rc, out_off(i, j, r));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if constexpr (kInt) {
+                        const uint32_t v = (uint32_t)p.alpha_i * (uint32_t)acc[i][j][r] +
+                                           (uint32_t)p.beta_i * (uint32_t)cv[r];
+                        Out<OUT>::store(rd, out_off(i, j, r), (int)v);
+                    } else {
+                        // one rounding of beta * c, then alpha * acc + (beta * c) fused
+                        Out<OUT>::store(rd, out_off(i, j, r),
+                                        __builtin_fmaf(p.alpha_f, acc[i][j][r], p.beta_f * cv[r]));
+                    }
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if constexpr (kInt)
+                        Out<OUT>::store(rd, out_off(i, j, r), (int)((uint32_t)p.alpha_i * (uint32_t)acc[i][j][r]));
+                    else
+                        Out<OUT>::store(rd, out_off(i, j, r), p.alpha_f * acc[i][j][r]);
+                }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------------------
 template <int IN, int OUT, bool TA, bool TB, int BM, int BN>
@@ -780,56 +840,8 @@ void gemm_kernel(Params p) {
     wait_vmem<0>();  // no direct load into LDS is left in flight when the workgroup ends
     drain_mfma(acc);
 
-    // ---- epilogue: D = alpha * acc + beta * C, masked to m x n
-    constexpr int OB = Out<OUT>::kBytes;
-    const int64_t tile_off = ((int64_t)m0 * p.ldc + n0) * OB;
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.D + tile_off);
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const char *)(p.read_c ? p.C : p.D) + tile_off);
-    const uint32_t ldc_b = (uint32_t)(p.ldc * OB);
-    // accumulator register r of block (i, j): row 16 i + 4 (lane / 16) + r, column 16 j + lane % 16
-    const int row_base = wm * (BM / 2) + 4 * (lane / 16);
-    const int col_base = wn * (BN / 2) + (lane % 16);
-    // byte offset of accumulator element r of block (i, j), or an out-of-range offset
-    auto out_off = [&](int i, int j, int r) -> uint32_t {
-        const int row = row_base + i * 16 + r;
-        const int col = col_base + j * 16;
-        const bool ok = full_mn || (row < m_left && col < n_left);
-        return ok ? (uint32_t)row * ldc_b + (uint32_t)col * OB : kOobOffset;
-    };
-    if (p.read_c) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                decltype(Out<OUT>::load(rc, 0)) cv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) cv[r] = Out<OUT>::load(rc, out_off(i, j, r));
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if constexpr (IN == IN_I8) {
-                        const uint32_t v = (uint32_t)p.alpha_i * (uint32_t)acc[i][j][r] +
-                                           (uint32_t)p.beta_i * (uint32_t)cv[r];
-                        Out<OUT>::store(rd, out_off(i, j, r), (int)v);
-                    } else {
-                        // one rounding of beta * c, then alpha * acc + (beta * c) fused
-                        Out<OUT>::store(rd, out_off(i, j, r),
-                                        __builtin_fmaf(p.alpha_f, acc[i][j][r], p.beta_f * cv[r]));
-                    }
-                }
-            }
-    } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if constexpr (IN == IN_I8)
-                        Out<OUT>::store(rd, out_off(i, j, r), (int)((uint32_t)p.alpha_i * (uint32_t)acc[i][j][r]));
-                    else
-                        Out<OUT>::store(rd, out_off(i, j, r), p.alpha_f * acc[i][j][r]);
-                }
-    }
+    // ---- epilogue
+    store_tile<IN == IN_I8, OUT, FM, FN, BM, BN>(p, acc, m0, n0, wm, wn, lane, full_mn, m_left, n_left);
 }
 
 // Host-side launcher of one instance.
@@ -850,6 +862,15 @@ hipError_t launch_fp8_fp8(int out, bool ta, bool tb, int tile, const Params &p, 
 hipError_t launch_fp8_bf8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
 hipError_t launch_bf8_fp8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
 hipError_t launch_bf8_bf8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
+// 2:4 structured-sparse A (sp24.hip): A's kept values (m x k/2, lda) in Params::A, their
+// indices (2 bits per kept value, in k order; m rows of ld_meta bytes) in meta.
+constexpr int kSpTileM = 256, kSpTileN = 128;
+struct SpParams {
+    Params p;
+    const void *meta;
+    int64_t ld_meta;
+};
+hipError_t launch_sp24(int in, int out, bool tb, const SpParams &sp, hipStream_t stream);
 // BF16 pieces of an FP32 operand for the three-product GEMM (bf16x3.hip).
 hipError_t launch_split_bf16x3(const float *in, int64_t rows, int64_t cols, int64_t ld_in,
                                void *out, int64_t ld_out, bool k_along_cols, int pieces,

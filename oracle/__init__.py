@@ -102,6 +102,13 @@ def _load() -> ctypes.CDLL:
         lib.oracle_gemm_fp8_points.argtypes = lib.oracle_gemm_fp_points.argtypes
         lib.oracle_gemm_fp8_full.restype = i32
         lib.oracle_gemm_fp8_full.argtypes = lib.oracle_gemm_fp_full.argtypes
+        lib.oracle_gemm_sp24_points.restype = i32
+        lib.oracle_gemm_sp24_points.argtypes = [i32, i64, dbl, vp, i32, i64, vp, i64, vp, i64, dbl,
+                                                vp, i32, i64, i64, vp, vp, vp, vp, vp]
+        lib.oracle_gemm_sp24_mfma_points.restype = i32
+        lib.oracle_gemm_sp24_mfma_points.argtypes = [i32, i64, flt, vp, i32, i64, vp, i64, vp, i64,
+                                                     flt, vp, i32, i64, i32, i32, i32, i32, i64,
+                                                     vp, vp, vp]
         lib.oracle_num_threads.restype = i32
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -380,6 +387,81 @@ def bf16x3_bound(S: np.ndarray, k: int, alpha: float, bc: np.ndarray) -> np.ndar
     keff = k3 if _is_pow2_or_zero(alpha) else k3 + 1
     return (a * S * (BF16X3_PRODUCT_ERROR + keff * 2.0 ** -23 * (1.0 + 2.0 ** -7))
             + 2.0 ** -23 * np.abs(bc) + a * max(k - 1, 0) * 2.0 ** -53 * S + 1e-300)
+
+
+def gemm_sp24(transb: bool, m: int, n: int, k: int, alpha: float, Ac: np.ndarray, atype: str,
+              lda: int, meta: np.ndarray, ld_meta: int, B: np.ndarray, ldb: int, beta: float,
+              C: Optional[np.ndarray], ctype: str, ldc: int,
+              points: Optional[tuple] = None) -> FpReference:
+    """2:4 structured-sparse A (kept values Ac, metadata meta), dense B of the same type:
+    exact products, double sums, as gemm_fp (mpgemm_oracle.c, oracle_gemm_sp24_points)."""
+    _check_storage("A", Ac, atype)
+    _check_storage("B", B, atype)
+    if beta != 0.0:
+        _check_storage("C", C, ctype)
+    else:
+        C = None
+    meta = np.ascontiguousarray(meta, dtype=np.uint8)
+    if points is None:
+        ii, jj = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+        ii, jj = ii.reshape(-1), jj.reshape(-1)
+    else:
+        ii, jj = points
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    v = np.empty(ii.shape, np.float64)
+    S = np.empty(ii.shape, np.float64)
+    bc = np.empty(ii.shape, np.float64)
+    rc = _load().oracle_gemm_sp24_points(int(bool(transb)), k, float(alpha), _ptr(Ac),
+                                         _CODES[atype], lda, meta.ctypes.data, ld_meta, _ptr(B),
+                                         ldb, float(beta), _ptr(C), _CODES[ctype], ldc, ii.size,
+                                         ii.ctypes.data, jj.ctypes.data, v.ctypes.data,
+                                         S.ctypes.data, bc.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"sparse oracle rejected type {atype}")
+    if points is None:
+        v, S, bc = v.reshape(m, n), S.reshape(m, n), bc.reshape(m, n)
+    return FpReference(v, S, bc)
+
+
+# Kept products per block of the sparse matrix cores (v_smfmac 16x16x64 FP16/BF16): eight, i.e.
+# sixteen logical k, with the dense window and sum rules -- measured on gfx950.
+SP24_BLOCK = 8
+
+
+def gemm_sp24_mfma(transb: bool, m: int, n: int, k: int, alpha: float, Ac: np.ndarray,
+                   atype: str, lda: int, meta: np.ndarray, ld_meta: int, B: np.ndarray, ldb: int,
+                   beta: float, C: Optional[np.ndarray], ctype: str, ldc: int, out_fmt: str,
+                   points: Optional[tuple] = None, nblk: int = SP24_BLOCK,
+                   frac: int = MFMA_FRAC, sum_bits: int = MFMA_SUM_BITS) -> np.ndarray:
+    """The block-FMA model applied to the 2:4 sparse GEMM's kept products in kept order
+    (mpgemm_oracle.c, oracle_gemm_sp24_mfma_points): output patterns in ``out_fmt``."""
+    _check_storage("A", Ac, atype)
+    _check_storage("B", B, atype)
+    if beta != 0.0:
+        _check_storage("C", C, ctype)
+    else:
+        C = None
+    meta = np.ascontiguousarray(meta, dtype=np.uint8)
+    if points is None:
+        ii, jj = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+        ii, jj = ii.reshape(-1), jj.reshape(-1)
+    else:
+        ii, jj = points
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    odt = np.uint32 if out_fmt == "f32" else np.uint16
+    D = np.empty(ii.shape, odt)
+    rc = _load().oracle_gemm_sp24_mfma_points(
+        int(bool(transb)), k, float(np.float32(alpha)), _ptr(Ac), _CODES[atype], lda,
+        meta.ctypes.data, ld_meta, _ptr(B), ldb, float(np.float32(beta)), _ptr(C), _CODES[ctype],
+        ldc, _CODES[out_fmt], int(nblk), int(frac), int(sum_bits), ii.size, ii.ctypes.data,
+        jj.ctypes.data, D.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"sparse block model rejected a={atype} c={ctype} out={out_fmt}")
+    if points is None:
+        D = D.reshape(m, n)
+    return D.view(np.float32) if out_fmt == "f32" else D
 
 
 def gemm_int(transa: bool, transb: bool, m: int, n: int, k: int, alpha: int,

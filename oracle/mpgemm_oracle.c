@@ -782,3 +782,98 @@ int oracle_gemm_fp8_full(int transa, int transb, int64_t m, int64_t n, int64_t k
                       &S[i * n + j], &bc[i * n + j]);
     return 0;
 }
+
+/* ======================================================================================
+ * 2:4 structured-sparse A (the page "稀疏张量核心加速模板计算的技术解析", sparse tensor cores for
+ * stencil computation, sections 1.2.1 and
+ * 1.3.2: at most two nonzeros per group of 4 consecutive k, kept values plus 2 bits of
+ * metadata each).  D(i, c) = alpha * sum_j Ac(i, j) * B(4 (j / 2) + idx(i, j), c)
+ * (+ beta * C(i, c)), idx(i, j) = bits 2 (j % 4) .. +1 of meta byte (i, j / 4).
+ * ====================================================================================== */
+static void sp24_point(const double *tab, int transb, int64_t k, double alpha,
+                       const uint16_t *Ac, int64_t lda, const uint8_t *meta, int64_t ld_meta,
+                       const uint16_t *B, int64_t ldb, double beta, const void *C, int ctype,
+                       int64_t ldc, int64_t i, int64_t c, double *v, double *S, double *bc)
+{
+    double s = 0.0, sa = 0.0;
+    for (int64_t j = 0; j < k / 2; ++j) {
+        const int idx = (meta[i * ld_meta + j / 4] >> (2 * (j % 4))) & 3;
+        const int64_t kk = 4 * (j / 2) + idx;
+        const double prod = tab[Ac[i * lda + j]] * tab[B[b_index(transb, ldb, kk, c)]];
+        s += prod;
+        sa += fabs(prod);
+    }
+    double betac = 0.0, out;
+    if (beta == 0.0) {
+        out = alpha * s;
+    } else {
+        betac = beta * c_elem(C, ctype, i * ldc + c);
+        out = alpha * s + betac;
+    }
+    *v = out;
+    *S = sa;
+    *bc = betac;
+}
+
+int oracle_gemm_sp24_points(int transb, int64_t k, double alpha, const void *Ac, int atype,
+                            int64_t lda, const void *meta, int64_t ld_meta, const void *B,
+                            int64_t ldb, double beta, const void *C, int ctype, int64_t ldc,
+                            int64_t npts, const int64_t *ii, const int64_t *jj, double *v,
+                            double *S, double *bc)
+{
+    if (atype != ORC_F16 && atype != ORC_BF16)
+        return -1;
+    double *tab = malloc(65536 * sizeof(double));
+    if (!tab)
+        return -2;
+    fill_table16(tab, atype);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < npts; ++t)
+        sp24_point(tab, transb, k, alpha, (const uint16_t *)Ac, lda, (const uint8_t *)meta,
+                   ld_meta, (const uint16_t *)B, ldb, beta, C, ctype, ldc, ii[t], jj[t], &v[t],
+                   &S[t], &bc[t]);
+    free(tab);
+    return 0;
+}
+
+/* Block-model result of the 2:4 sparse GEMM at the points: the kept products
+ * Ac(i, j) * B(4 (j / 2) + idx(i, j), c), in kept order j, go through the same block-FMA
+ * accumulation as the dense model (blocks of nblk kept products), then the dense epilogue. */
+int oracle_gemm_sp24_mfma_points(int transb, int64_t k, float alpha, const void *Ac, int atype,
+                                 int64_t lda, const void *meta, int64_t ld_meta, const void *B,
+                                 int64_t ldb, float beta, const void *C, int ctype, int64_t ldc,
+                                 int otype, int nblk, int frac, int sum_bits, int64_t npts,
+                                 const int64_t *ii, const int64_t *jj, void *D)
+{
+    if (!mfma_args_ok(atype, atype, ctype, otype, nblk, frac, sum_bits) || k % 4)
+        return -1;
+    const int mb = mbits_of(atype);
+    const int64_t kh = k / 2;
+    int failed = 0;
+#pragma omp parallel
+    {
+        fp_parts *row = malloc((size_t)(kh > 0 ? kh : 1) * sizeof(fp_parts));
+        fp_parts *col = malloc((size_t)(kh > 0 ? kh : 1) * sizeof(fp_parts));
+        if (!row || !col) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < npts; ++t) {
+            if (!row || !col)
+                continue;
+            const int64_t i = ii[t], c = jj[t];
+            for (int64_t j = 0; j < kh; ++j) {
+                const int idx = (((const uint8_t *)meta)[i * ld_meta + j / 4] >> (2 * (j % 4))) & 3;
+                row[j] = parts16(((const uint16_t *)Ac)[i * lda + j], atype);
+                col[j] = parts16(((const uint16_t *)B)[b_index(transb, ldb, 4 * (j / 2) + idx, c)],
+                                 atype);
+            }
+            const float acc = mfma_dot(row, col, kh, mb, nblk, frac, sum_bits);
+            store_out(D, otype, t, mfma_epilogue(acc, alpha, beta, C, ctype, ldc, i, c));
+        }
+        free(row);
+        free(col);
+    }
+    return failed ? -2 : 0;
+}

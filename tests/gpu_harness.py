@@ -176,3 +176,65 @@ def run_bf16x3(inp: Inputs, in_place: bool = False, workspace_bytes: Optional[in
         ws = ws[ws_ptr - base: ws_ptr - base + size]
     res = GpuResult(D=D.view(np.float32).reshape(w.m, w.ldc), guard_ok=guard_ok)
     return res, ws, st
+
+
+def run_sp24(inp: Inputs, in_place: bool = False, check: bool = True):
+    """Run mpgemm_run_sp24 on inp (2:4 sparse A: kept values inp.A, metadata inp.meta).
+    D carries GUARD_ROWS sentinel rows; returns (GpuResult, status)."""
+    w = inp.w
+    ob = ELEM_BYTES[w.out_type]
+    dA = mp.device_buffer(inp.A, w.in_type)
+    dM = mp.device_buffer(inp.meta, "i8")
+    dB = mp.device_buffer(inp.B, w.in_type)
+    d_bytes = (w.m + GUARD_ROWS) * w.ldc * ob
+    if in_place:
+        cbuf = np.concatenate([inp.C.view(np.uint8).reshape(-1),
+                               np.full(GUARD_ROWS * w.ldc * ob, SENTINEL, np.uint8)])
+        dC = dD = mp.device_buffer(cbuf, "i8")
+    else:
+        dC = mp.device_buffer(inp.C, w.out_type) if inp.C is not None else None
+        dD = torch.full((d_bytes,), SENTINEL, dtype=torch.uint8, device="cuda")
+    st = mp.mpgemm_run_sp24(handle().h, w.transb, w.m, w.n, w.k, w.alpha, dA, w.in_type, w.lda,
+                            dM, w.ld_meta, dB, w.in_type, w.ldb, w.beta, dC, w.out_type, w.ldc,
+                            dD, check=check)
+    torch.cuda.synchronize()
+    raw = dD.cpu().numpy()
+    D = raw[: w.m * w.ldc * ob].view(np.uint8)
+    guard_ok = bool(np.all(raw[w.m * w.ldc * ob:] == SENTINEL))
+    if w.ldc > w.n:
+        pad = D.reshape(w.m, w.ldc * ob)[:, w.n * ob:]
+        if in_place:
+            guard_ok &= bool(np.array_equal(pad, inp.C.view(np.uint8).reshape(w.m, w.ldc * ob)[:, w.n * ob:]))
+        else:
+            guard_ok &= bool(np.all(pad == SENTINEL))
+    storage = {"f16": np.uint16, "bf16": np.uint16, "f32": np.float32}[w.out_type]
+    return GpuResult(D=D.view(storage).reshape(w.m, w.ldc), guard_ok=guard_ok), st
+
+
+def sp24_ref(inp: Inputs, points=None):
+    w = inp.w
+    return oracle.gemm_sp24(w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda, inp.meta,
+                            w.ld_meta, inp.B, w.ldb, w.beta, inp.C, w.out_type, w.ldc,
+                            points=points)
+
+
+def compare_sp24(inp: Inputs, res: GpuResult, exact: bool = False, points=None):
+    """The sparse output against the oracle: exact, or within the FP bound over k/2 products."""
+    w = inp.w
+    D = res.D[:, : w.n]
+    if points is not None:
+        D = D[points[0], points[1]]
+    return oracle.check_fp(np.ascontiguousarray(D), w.out_type, sp24_ref(inp, points),
+                           max(w.k // 2, 1), w.alpha, exact=exact)
+
+
+def compare_sp24_model(inp: Inputs, res: GpuResult, points=None):
+    """Bitwise comparison of the sparse output with the sparse block model."""
+    w = inp.w
+    D = res.D[:, : w.n]
+    if points is not None:
+        D = D[points[0], points[1]]
+    ref = oracle.gemm_sp24_mfma(w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda,
+                                inp.meta, w.ld_meta, inp.B, w.ldb, w.beta, inp.C, w.out_type,
+                                w.ldc, w.out_type, points=points)
+    return oracle.check_bits(np.ascontiguousarray(D), w.out_type, ref)

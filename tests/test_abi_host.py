@@ -175,3 +175,53 @@ def test_fp8_type_matrix():
     assert chk(a_type="e4m3", b_type="f16") == ST["NOT_SUPPORTED"]
     assert chk(a_type="e4m3", b_type="e4m3", lda=72) == ST["NOT_SUPPORTED"]     # 16-element rows
     assert mp.mpgemm_tile_shape(256, 256, "e4m3") == (128, 128)
+
+
+def chk_sp(**kw):
+    a = dict(transb=True, m=300, n=200, k=256, alpha=1.0, Ac=P, a_type="f16", lda=128, meta=P,
+             ld_meta=32, B=P, b_type="f16", ldb=256, beta=0.0, C=None, c_type="f32", ldc=200,
+             D=P, compute_type="f32")
+    a.update(kw)
+    return mp.mpgemm_check_sp24(a["transb"], a["m"], a["n"], a["k"], a["alpha"], a["Ac"],
+                                a["a_type"], a["lda"], a["meta"], a["ld_meta"], a["B"],
+                                a["b_type"], a["ldb"], a["beta"], a["C"], a["c_type"], a["ldc"],
+                                a["D"], a["compute_type"])
+
+
+def test_sp24_contract():
+    assert chk_sp() == ST["SUCCESS"]
+    assert chk_sp(transb=False, ldb=200) == ST["SUCCESS"]
+    for a, c in (("f16", "f16"), ("bf16", "f32"), ("bf16", "bf16")):
+        assert chk_sp(a_type=a, b_type=a, c_type=c) == ST["SUCCESS"]
+    # types outside the matrix
+    assert chk_sp(a_type="f16", b_type="bf16") == ST["NOT_SUPPORTED"]
+    assert chk_sp(c_type="bf16") == ST["NOT_SUPPORTED"]
+    assert chk_sp(a_type="i8", b_type="i8", c_type="i32", compute_type="i32") == ST["NOT_SUPPORTED"]
+    assert chk_sp(a_type="e4m3", b_type="e4m3") == ST["NOT_SUPPORTED"]
+    assert chk_sp(compute_type="i32") == ST["NOT_SUPPORTED"]
+    # k a multiple of 128; k = 0 allowed (D = beta C), with null operands
+    assert chk_sp(k=200, lda=104, ld_meta=32, ldb=200) == ST["NOT_SUPPORTED"]
+    assert chk_sp(k=0, lda=8, ld_meta=16, ldb=8, Ac=None, meta=None, B=None) == ST["SUCCESS"]
+    # leading-dimension minimums and alignment
+    assert chk_sp(lda=120) == ST["INVALID_VALUE"]
+    assert chk_sp(ld_meta=16) == ST["INVALID_VALUE"]          # 256 / 8 = 32 bytes per row
+    assert chk_sp(ldb=200) == ST["INVALID_VALUE"]
+    assert chk_sp(ldc=199) == ST["INVALID_VALUE"]
+    assert chk_sp(lda=132) == ST["NOT_SUPPORTED"]             # 264-byte rows
+    assert chk_sp(ld_meta=40) == ST["NOT_SUPPORTED"]
+    assert chk_sp(Ac=P + 8) == ST["NOT_SUPPORTED"]
+    assert chk_sp(meta=P + 4) == ST["NOT_SUPPORTED"]
+    # nulls, negative sizes, empty outputs
+    assert chk_sp(meta=None) == ST["INVALID_VALUE"]
+    assert chk_sp(D=None) == ST["INVALID_VALUE"]
+    assert chk_sp(beta=1.0) == ST["INVALID_VALUE"]            # C needed
+    assert chk_sp(beta=1.0, C=P) == ST["SUCCESS"]
+    assert chk_sp(m=-1) == ST["INVALID_VALUE"]
+    assert chk_sp(m=0, Ac=None, meta=None, B=None, D=None) == ST["SUCCESS"]
+    # strides past what 32-bit tile offsets reach
+    assert chk_sp(lda=1 << 22) == ST["NOT_SUPPORTED"]
+
+
+def test_sp24_rejects_unknown_handles():
+    assert mp.mpgemm_run_sp24(0x1000, True, 8, 8, 128, 1.0, P, "f16", 64, P, 16, P, "f16", 128,
+                              0.0, None, "f32", 8, P, stream=0, check=False) == ST["NOT_INITIALIZED"]
