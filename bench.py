@@ -118,7 +118,7 @@ def time_gemm(w, steps: int, warmup: int):
     ev1.record(stream)
     ev1.synchronize()
     kern_ms = ev0.elapsed_time(ev1) / steps
-    tile = (256, 128) if w.sparse24 else mp.mpgemm_tile_shape(w.m, w.n, w.in_type)
+    tile = (256, 256) if w.sparse24 else mp.mpgemm_tile_shape(w.m, w.n, w.in_type)
     h.close()
     return wall_ms, kern_ms, tile
 

@@ -864,7 +864,7 @@ hipError_t launch_bf8_fp8(int out, bool ta, bool tb, int tile, const Params &p, 
 hipError_t launch_bf8_bf8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
 // 2:4 structured-sparse A (sp24.hip): A's kept values (m x k/2, lda) in Params::A, their
 // indices (2 bits per kept value, in k order; m rows of ld_meta bytes) in meta.
-constexpr int kSpTileM = 256, kSpTileN = 128;
+constexpr int kSpTileM = 256, kSpTileN = 256;
 struct SpParams {
     Params p;
     const void *meta;

@@ -3,21 +3,29 @@
 //   D = alpha * A * op(B) + beta * C,   A: m x k with at most 2 nonzeros in every group of 4
 //                                        consecutive k, given compressed (values + indices)
 //
-// Sparse tensor cores as the page "稀疏张量核心加速模板计算的技术解析" (sparse tensor cores for stencil
-// computation) describes them in sections 1.2.1 and 1.3.2: a 2:4 sparse
-// operand is held as its kept values (half of k) plus 2 bits of metadata per kept value (its
-// position within its group of 4), and the matrix instruction skips the zeros.  Here the
-// instruction is v_smfmac_f32_16x16x64_{f16,bf16}: a 16 x 16 output block over 64 logical k
-// from A's kept values (lane group g: the 8 kept values of k 16 g .. 16 g + 15, 16 bytes),
-// B's 64 k-rows (two 32-k fragments of the dense layout, 32 bytes) and a 16-bit index (2 bits
-// per kept value, low half of the register) -- lane layouts measured on gfx950.
+// Sparse tensor cores as the page "稀疏张量核心加速模板计算的技术解析" (sparse tensor cores
+// for stencil computation) describes them in sections 1.2.1 and 1.3.2: a 2:4 sparse operand is
+// held as its kept values (half of k) plus 2 bits of metadata per kept value (its position
+// within its group of 4), and the matrix instruction skips the zeros.  Here the instruction is
+// v_smfmac_f32_16x16x64_{f16,bf16}: a 16 x 16 output block over 64 logical k from A's kept
+// values (lane group g: the 8 kept values of k 16 g .. 16 g + 15, 16 bytes), B's 64 k-rows (two
+// 32-k fragments of the dense layout, 32 bytes) and a 16-bit index (2 bits per kept value, low
+// half of the register) -- lane layouts measured on gfx950.
 //
-// The pipeline is the dense kernel's (mpgemm_kernel.hpp): direct-to-LDS loads of each stage
-// into one of two LDS buffers, fragments of the next k step read during the current one, one
-// barrier per stage.  A stage is 128 logical k: A's 64 kept values per row (128 bytes, the
-// dense K-contiguous operand geometry), B's 128 k-rows as two dense stages of 64, and the
-// metadata's 16 bytes per row (one 1 KB load per wave).  The tile is 256 x 128 (LDS 136 KB);
-// k must be a multiple of 128 (no K tail), m and n are arbitrary.
+// One sparse instruction does the useful work of one dense 16 x 16 x 32 in the same issue
+// time, so per MFMA cycle the sparse loop needs about twice the bytes of the dense kernel.  The
+// loop is therefore built around the global -> LDS stream:
+//   * tile 256 x 256 (2 x 2 waves of 128 x 128), the largest the accumulators allow;
+//   * a stage is one sparse k step of 64 logical k: A's 32 kept values per row (64 bytes),
+//     B's 64 k-rows (the dense kernel's 16-bit B stage) -- 48 KB -- plus, every second stage,
+//     16 metadata bytes per row covering two stages (4 KB);
+//   * an LDS ring of three stages (and two metadata pairs), so that two stages of loads are in
+//     flight while the third is multiplied: each iteration waits only for the older one;
+//   * all fragments of the next stage are read during the current one; a B block's register
+//     is refilled right after its last MFMA, and B block 7 alternates between two registers so
+//     that its refill is not the last instruction of the iteration.
+// LDS: [A ring 3 x 16 KB | B ring 3 x 32 KB | metadata 2 x 4 KB] = 152 KB.  k must be a
+// multiple of 128 (an even number of stages, no K tail); m and n are arbitrary.
 #include "mpgemm_kernel.hpp"
 
 namespace mpg {
@@ -37,6 +45,40 @@ template <> struct SMma<IN_BF16> {
 };
 
 typedef __attribute__((address_space(3))) unsigned short lds_u16;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// A's kept values, K-contiguous: a stage holds 256 rows of 64 bytes (row r at r * 64, its
+// 16-byte chunk c at chunk position c ^ swz(r)).  A fragment read (16 rows x 64 bytes; lanes
+// 0-31 take chunks 0-1 of rows 0-15, lanes 32-63 chunks 2-3) is served 32 lanes at a time over
+// 128 four-byte banks: rows r and r + 8 share a bank base, so rows 8-15 swap chunk pairs.
+struct KeptA {
+    static constexpr int kRows = 256;
+    static constexpr int kStageBytes = kRows * 64;     // 16 KB
+    static constexpr int kSlots = kStageBytes / 4096;  // 1 KB loads per wave per stage
+    uint32_t voff[kSlots];
+    uint32_t r_off;
+    static __device__ __forceinline__ int swz(int r) { return ((r >> 3) & 1) << 1; }
+    // Load slot i of wave w, lane l fills LDS bytes i * 4096 + w * 1024 + l * 16 of the stage:
+    // row 64 i + 16 w + l / 4, physical chunk l % 4.  Rows past the matrix repeat its last row.
+    __device__ __forceinline__ void init(int wave, int lane, int64_t lda, int m_left) {
+        const uint32_t row_bytes = (uint32_t)(lda * 2);
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            const int r = 64 * i + 16 * wave + lane / 4;
+            const int c = (lane % 4) ^ swz(r);
+            voff[i] = (uint32_t)min(r, m_left - 1) * row_bytes + 16u * (uint32_t)c;
+        }
+        const int u = lane % 16, g = lane / 16;
+        r_off = (uint32_t)(u * 64 + 16 * (g ^ swz(u)));
+    }
+    __device__ __forceinline__ void load(i32x4 rs, uint32_t lds_stage_w, int i) const {
+        dma16(rs, voff[i], 0u, lds_stage_w + (uint32_t)i * 4096u);
+    }
+    // 16-byte operand of 16-row block `blk` (the lane's row blk * 16 + lane % 16)
+    __device__ __forceinline__ u32x4 frag(const lds_char *stage, int blk) const {
+        return *(const lds_u32x4 *)(stage + blk * 1024 + r_off);
+    }
+};
 
 }  // namespace
 
@@ -46,17 +88,16 @@ void sp24_kernel(SpParams sp) {
     const Params &p = sp.p;
     constexpr int BM = kSpTileM, BN = kSpTileN;
     constexpr int FM = BM / 32, FN = BN / 32;       // 16-wide blocks per wave (2 x 2 waves)
-    using OpA = Operand<2, true, BM / 32>;          // kept values: K-contiguous, 64 per stage
-    using OpB = Operand<2, TB, BN / 32>;            // each 64-k-row half of a stage of B
-    constexpr int A_BYTES = OpA::kStageBytes;       // 32 KB
-    constexpr int BH_BYTES = OpB::kStageBytes;      // 16 KB
-    constexpr int B_BYTES = 2 * BH_BYTES;
-    constexpr int M_BYTES = BM * 16;                // metadata: 16 bytes per row per stage
-    constexpr int B_BASE = kBuffers * A_BYTES, M_BASE = B_BASE + kBuffers * B_BYTES;
-    constexpr int kLoads = OpA::kSlots + 2 * OpB::kSlots + 1;   // per wave per stage
+    using OpB = Operand<2, TB, BN / 32>;            // 64 k-rows of B per stage
+    constexpr int kRing = 3;
+    constexpr int A_STAGE = KeptA::kStageBytes;     // 16 KB
+    constexpr int B_STAGE = OpB::kStageBytes;       // 32 KB
+    constexpr int M_PAIR = BM * 16;                 // metadata of two stages: 16 bytes per row
+    constexpr int B_BASE = kRing * A_STAGE, M_BASE = B_BASE + kRing * B_STAGE;
+    constexpr int kLoadsAB = KeptA::kSlots + OpB::kSlots;   // 12 per wave per stage (+1 metadata)
+    static_assert(FM == 8 && FN == 8, "tile");
 
-    // LDS: [A0 | A1 | B0 (k-rows 0-63, 64-127) | B1 | M0 | M1]
-    __shared__ __attribute__((aligned(16))) char smem_raw[M_BASE + kBuffers * M_BYTES];
+    __shared__ __attribute__((aligned(16))) char smem_raw[M_BASE + 2 * M_PAIR];
     lds_char *smem = (lds_char *)smem_raw;
 
     const int tid = threadIdx.x;
@@ -68,44 +109,41 @@ void sp24_kernel(SpParams sp) {
     const int m_left = p.m - m0, n_left = p.n - n0;
     const bool full_mn = (m_left >= BM) && (n_left >= BN);
 
-    OpA opa;
-    OpB opb_lo, opb_hi;
-    opa.init(wave, lane, p.lda, m_left, 0u);
-    opb_lo.init(wave, lane, p.ldb, n_left, (uint32_t)B_BASE);
-    opb_hi.init(wave, lane, p.ldb, n_left, (uint32_t)(B_BASE + BH_BYTES));
-    const int nk = p.k / 128;                        // stages (k is a multiple of 128)
+    KeptA opa;
+    OpB opb;
+    opa.init(wave, lane, p.lda, m_left);
+    opb.init(wave, lane, p.ldb, n_left, 0u);
+    const int nk = p.k / 64;                         // stages (even: k is a multiple of 128)
+    const int np = nk / 2;                           // metadata pairs
 
-    // Stage cursors (see StageCursor): the exact readable end of each operand bounds the
-    // last stage.  A's rows hold k / 2 kept values; B's two halves are 64 k-rows apart.
-    StageCursor ca, cb_lo, cb_hi, cm;
+    // Stage cursors: the exact readable end of each operand bounds its last stage.
+    StageCursor ca, cb, cm;
     {
-        const int64_t kc = p.k / 2;
-        const int64_t end_a = (int64_t)(p.m - 1) * p.lda * 2 + ((kc * 2 + 15) & ~(int64_t)15);
+        const int64_t end_a = (int64_t)(p.m - 1) * p.lda * 2 + (int64_t)p.k;   // k/2 kept x 2 B
         const int64_t rb = TB ? p.n : p.k, clb = TB ? p.k : p.n;
         const int64_t end_b = (rb - 1) * p.ldb * 2 + ((clb * 2 + 15) & ~(int64_t)15);
-        const int64_t end_m = (int64_t)(p.m - 1) * sp.ld_meta + (((int64_t)p.k / 8 + 15) & ~(int64_t)15);
+        const int64_t end_m = (int64_t)(p.m - 1) * sp.ld_meta + (int64_t)p.k / 8;
         const int64_t off_a = (int64_t)m0 * p.lda * 2;
         const int64_t off_b = TB ? (int64_t)n0 * p.ldb * 2 : (int64_t)n0 * 2;
-        const int64_t half_b = TB ? 128 : (int64_t)64 * p.ldb * 2;   // k-rows 64..127 of a stage
         const int64_t off_m = (int64_t)m0 * sp.ld_meta;
-        ca.step = kStageKBytes;
-        cb_lo.step = cb_hi.step = TB ? 256 : (int64_t)128 * p.ldb * 2;
+        ca.step = 64;
+        cb.step = TB ? 128 : (int64_t)64 * p.ldb * 2;
         cm.step = 16;
         ca.base = (uint64_t)p.A + (uint64_t)off_a;
-        cb_lo.base = (uint64_t)p.B + (uint64_t)off_b;
-        cb_hi.base = cb_lo.base + (uint64_t)half_b;
+        cb.base = (uint64_t)p.B + (uint64_t)off_b;
         cm.base = (uint64_t)sp.meta + (uint64_t)off_m;
-        auto last = [&](int64_t end, int64_t off, int64_t step) {
-            const int64_t l = end - off - (int64_t)(nk > 0 ? nk - 1 : 0) * step;
+        auto last = [&](int64_t end, int64_t off, int64_t step, int count) {
+            const int64_t l = end - off - (int64_t)(count > 0 ? count - 1 : 0) * step;
             return (int)(l < 0 ? 0 : (l > kNumRecords ? kNumRecords : l));
         };
-        ca.last_records = last(end_a, off_a, ca.step);
-        cb_lo.last_records = last(end_b, off_b, cb_lo.step);
-        cb_hi.last_records = last(end_b, off_b + half_b, cb_hi.step);
-        cm.last_records = last(end_m, off_m, cm.step);
+        ca.last_records = last(end_a, off_a, ca.step, nk);
+        cb.last_records = last(end_b, off_b, cb.step, nk);
+        cm.last_records = last(end_m, off_m, cm.step, np);
     }
     // metadata load: lane l of wave w brings row 64 w + l (clamped to the last row)
     const uint32_t voff_m = (uint32_t)min(64 * wave + lane, m_left - 1) * (uint32_t)sp.ld_meta;
+    // metadata read: row wm * 128 + 16 i + lane % 16, lane group g's 8 positions (2 bytes)
+    const uint32_t m_lane = (uint32_t)((wm * (BM / 2) + lane % 16) * 16 + 2 * (lane / 16));
 
     f32x4 acc[FM][FN];
 #pragma unroll
@@ -114,101 +152,115 @@ void sp24_kernel(SpParams sp) {
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{};
 
     const uint32_t lds_w = (uint32_t)(uintptr_t)smem + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
-    i32x4 rs_a, rs_lo, rs_hi, rs_m;
-    auto next_rsrc = [&](int s) {
-        rs_a = ca.rsrc(s, nk);
+    i32x4 rs_a, rs_b, rs_m;
+    // Resources of stage t (the cursors then move on); `with_meta` for even t.
+    auto prep = [&](int t, auto meta_c) {
+        rs_a = ca.rsrc(t, nk);
         ca.advance();
-        rs_lo = cb_lo.rsrc(s, nk);
-        cb_lo.advance();
-        rs_hi = cb_hi.rsrc(s, nk);
-        cb_hi.advance();
-        rs_m = cm.rsrc(s, nk);
-        cm.advance();
-    };
-    auto load_slot = [&](int parity, int l) {
-        if (l < OpA::kSlots) {
-            opa.load(rs_a, lds_w + (uint32_t)(parity * A_BYTES), l);
-        } else if (l < OpA::kSlots + OpB::kSlots) {
-            opb_lo.load(rs_lo, lds_w + (uint32_t)(B_BASE + parity * B_BYTES), l - OpA::kSlots);
-        } else if (l < kLoads - 1) {
-            opb_hi.load(rs_hi, lds_w + (uint32_t)(B_BASE + parity * B_BYTES + BH_BYTES),
-                        l - OpA::kSlots - OpB::kSlots);
-        } else {
-            dma16(rs_m, voff_m, 0u, lds_w + (uint32_t)(M_BASE + parity * M_BYTES));
+        rs_b = cb.rsrc(t, nk);
+        cb.advance();
+        if constexpr (decltype(meta_c)::value) {
+            rs_m = cm.rsrc(t >> 1, np);
+            cm.advance();
         }
     };
+    // Load l of a stage into ring slot q (and metadata buffer mq): the metadata first when the
+    // stage carries it, then A's slots, then B's.
+    auto load_slot = [&](int q, int mq, auto meta_c, int l) {
+        constexpr bool kMeta = decltype(meta_c)::value;
+        if (kMeta && l == 0) {
+            dma16(rs_m, voff_m, 0u, lds_w + (uint32_t)(M_BASE + mq * M_PAIR));
+            return;
+        }
+        const int la = l - (kMeta ? 1 : 0);
+        if (la < KeptA::kSlots)
+            opa.load(rs_a, lds_w + (uint32_t)(q * A_STAGE), la);
+        else
+            opb.load(rs_b, lds_w + (uint32_t)(B_BASE + q * B_STAGE), la - KeptA::kSlots);
+    };
 
-    // Fragments of one k step (64 logical k): A's kept values, B's two 32-k fragments, the
-    // index.  Two sets: the next k step's are read during the current one.
+    // Fragments: A and the indices in two sets (this stage's, the next one's), B blocks 0-6 in
+    // one register each (refilled after their last use), B block 7 in two alternating ones.
     u32x4 fa[2][FM];
-    u32x8 fb[2][FN];
     uint32_t fi[2][FM];
-    // metadata of row (16 i + lane % 16) of this wave's rows, k step t, lane group g
-    const uint32_t m_lane = (uint32_t)((wm * (BM / 2) + lane % 16) * 16 + 2 * (lane / 16));
-    constexpr int kUnits = FM + 2 * FN + FM, kMf = FM * FN;
-    auto read_unit = [&](int set, int parity, int t, int u) {
-        if (u < FM) {
-            fa[set][u] = opa.frag(smem + parity * A_BYTES, wm * FM + u, t);
-        } else if (u < FM + 2 * FN) {
-            const int j = (u - FM) / 2, h = (u - FM) % 2;
-            const lds_char *st = smem + parity * B_BYTES;
-            set_half(fb[set][j], h, t == 0 ? opb_lo.frag(st, wn * FN + j, h) : opb_hi.frag(st, wn * FN + j, h));
-        } else {
-            const int i = u - FM - 2 * FN;
-            fi[set][i] = *(const lds_u16 *)(smem + M_BASE + parity * M_BYTES + m_lane + i * 256 + 8 * t);
-        }
+    u32x8 fb[FN - 1];
+    u32x8 fb7[2];
+    auto read_a = [&](int set, const lds_char *st, int i) { fa[set][i] = opa.frag(st, wm * FM + i); };
+    auto read_i = [&](int set, const lds_char *mst, int half, int i) {
+        fi[set][i] = *(const lds_u16 *)(mst + m_lane + i * 256 + 8 * half);
+    };
+    auto read_b = [&](u32x8 &dst, const lds_char *st, int j) {
+        set_half(dst, 0, opb.frag(st, wn * FN + j, 0));
+        set_half(dst, 1, opb.frag(st, wn * FN + j, 1));
     };
 
-    // One k step: FM x FN sparse MFMAs of fragment set `set`, each in its own fenced group
-    // with at most a few other instructions; the next k step's fragments are read spread over
-    // the MFMAs; in the second k step of a stage the loads of the stage two ahead.
-    auto k_step = [&](auto set_c, int rd_parity, int rd_t, int ld_parity, auto nl_c, auto &&hook) {
-        constexpr int set = decltype(set_c)::value, nl = decltype(nl_c)::value;
-        wait_lds<0>();
-        static_for<kMf>([&](auto idx_c) {
+    // Prologue: stages 0, 1, 2 queued (metadata pairs 0 and 1 with stages 0 and 2); wait for
+    // stage 0 and read its fragments.
+    using CT = std::integral_constant<bool, true>;
+    using CF = std::integral_constant<bool, false>;
+    prep(0, CT{});
+    static_for<kLoadsAB + 1>([&](auto l_c) { load_slot(0, 0, CT{}, decltype(l_c)::value); });
+    prep(1, CF{});
+    static_for<kLoadsAB>([&](auto l_c) { load_slot(1, 0, CF{}, decltype(l_c)::value); });
+    prep(2, CT{});
+    static_for<kLoadsAB + 1>([&](auto l_c) { load_slot(2, 1, CT{}, decltype(l_c)::value); });
+    wait_vmem<2 * kLoadsAB + 1>();
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        read_a(0, smem, i);
+        read_i(0, smem + M_BASE, 0, i);
+    }
+#pragma unroll
+    for (int j = 0; j < FN - 1; ++j) read_b(fb[j], smem + B_BASE, j);
+    read_b(fb7[0], smem + B_BASE, FN - 1);
+    wait_lds<0>();
+
+    // Iteration s (H = s & 1) multiplies stage s (ring slot q) out of registers, reads the
+    // fragments of stage s + 1 (ring slot q + 1) and queues the loads of stage s + 3 into slot
+    // q, whose last reads were waited for at the barrier.  Its first instructions wait for
+    // stage s + 1 (at most one stage's loads, 12, may still be in flight: those of stage s + 2,
+    // which has 13 when it carries metadata, so its first load is waited for too).
+    auto iteration = [&](int s, int q, auto h_c) {
+        constexpr int H = decltype(h_c)::value;
+        constexpr bool kMeta = H == 1;               // stage s + 3 even: it carries metadata
+        constexpr int kL = kLoadsAB + (kMeta ? 1 : 0);
+        const int qn = q == kRing - 1 ? 0 : q + 1;
+        wait_vmem<kLoadsAB>();
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        const lds_char *stA = smem + qn * A_STAGE;
+        const lds_char *stB = smem + B_BASE + qn * B_STAGE;
+        const lds_char *stM = smem + M_BASE + (((s + 1) >> 1) & 1) * M_PAIR;
+        const int mq = ((s + 3) >> 1) & 1;
+        static_for<FM * FN>([&](auto idx_c) {
             constexpr int idx = decltype(idx_c)::value;
-            constexpr int i = idx / FN, j = idx % FN;
-            SMma<IN>::run(fa[set][i], fb[set][j], fi[set][i], acc[i][j]);
-            hook(idx_c);
-            static_for<kUnits>([&](auto u_c) {
-                constexpr int u = decltype(u_c)::value;
-                constexpr int at = (u * kMf) / kUnits;
-                if constexpr (at == idx) read_unit(set ^ 1, rd_parity, rd_t, u);
-            });
-            static_for<nl>([&](auto l_c) {
+            constexpr int j = idx / FM, i = idx % FM;   // B-block-major
+            if constexpr (j < FN - 1)
+                SMma<IN>::run(fa[H][i], fb[j], fi[H][i], acc[i][j]);
+            else
+                SMma<IN>::run(fa[H][i], fb7[H], fi[H][i], acc[i][j]);
+            if constexpr (idx == 0) prep(s + 3, std::integral_constant<bool, kMeta>{});
+            if constexpr (idx == 1) read_b(fb7[H ^ 1], stB, FN - 1);
+            if constexpr (i == 2) read_a(H ^ 1, stA, j);
+            if constexpr (i == 3) read_i(H ^ 1, stM, (s + 1) & 1, j);
+            if constexpr (i == FM - 1 && j < FN - 1) read_b(fb[j], stB, j);
+            static_for<kL>([&](auto l_c) {
                 constexpr int l = decltype(l_c)::value;
-                constexpr int at = ((l * kMf) / (nl > 0 ? nl : 1) + 1) % kMf;
-                if constexpr (at == idx) load_slot(ld_parity, l);
+                constexpr int at = 4 + (l * 58) / kL;
+                if constexpr (at == idx) load_slot(q, mq, std::integral_constant<bool, kMeta>{}, l);
             });
             __builtin_amdgcn_sched_barrier(0);
         });
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
-    using CL = std::integral_constant<int, kLoads>;
-    auto stage_iter = [&](int s, auto par_c) {
-        constexpr int P = decltype(par_c)::value;
-        k_step(C0{}, P, 1, 0, C0{}, [&](auto idx_c) {
-            if constexpr (decltype(idx_c)::value == 1 % kMf) next_rsrc(s + 2);
-        });
-        wait_vmem<0>();  // this wave's loads of stage s + 1 have landed
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        k_step(C1{}, P ^ 1, 0, P, CL{}, [&](auto) {});
-    };
-
-    // Prologue: stages 0 and 1 queued, stage 0 waited for, the first k step's fragments read.
-    next_rsrc(0);
-    static_for<kLoads>([&](auto l_c) { load_slot(0, decltype(l_c)::value); });
-    next_rsrc(1);
-    static_for<kLoads>([&](auto l_c) { load_slot(1, decltype(l_c)::value); });
-    wait_vmem<kLoads>();
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kUnits; ++u) read_unit(0, 0, 0, u);
+    int q = 0;
     for (int s = 0; s < nk; s += 2) {
-        stage_iter(s, C0{});
-        stage_iter(s + 1, C1{});
+        iteration(s, q, C0{});
+        q = q == kRing - 1 ? 0 : q + 1;
+        iteration(s + 1, q, C1{});
+        q = q == kRing - 1 ? 0 : q + 1;
     }
     wait_vmem<0>();  // no direct load into LDS is left in flight when the workgroup ends
     drain_mfma(acc);
