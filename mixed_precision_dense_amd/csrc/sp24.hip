@@ -17,14 +17,15 @@
 // loop is therefore built around the global -> LDS stream:
 //   * tile 256 x 256 (2 x 2 waves of 128 x 128), the largest the accumulators allow;
 //   * a stage is one sparse k step of 64 logical k: A's 32 kept values per row (64 bytes),
-//     B's 64 k-rows (the dense kernel's 16-bit B stage) -- 48 KB -- plus, every second stage,
-//     16 metadata bytes per row covering two stages (4 KB);
-//   * an LDS ring of three stages (and two metadata pairs), so that two stages of loads are in
+//     B's 64 k-rows (the dense kernel's 16-bit B stage) -- 48 KB -- plus, every fourth stage,
+//     32 metadata bytes per row covering four stages (8 KB; two lanes per row, so one 32-byte
+//     request per row: the loop is bound by the L2 request rate, not by bytes);
+//   * an LDS ring of three stages (and two metadata quads), so that two stages of loads are in
 //     flight while the third is multiplied: each iteration waits only for the older one;
 //   * all fragments of the next stage are read during the current one; a B block's register
 //     is refilled right after its last MFMA, and B block 7 alternates between two registers so
 //     that its refill is not the last instruction of the iteration.
-// LDS: [A ring 3 x 16 KB | B ring 3 x 32 KB | metadata 2 x 4 KB] = 152 KB.  k must be a
+// LDS: [A ring 3 x 16 KB | B ring 3 x 32 KB | metadata 2 x 8 KB] = 160 KB.  k must be a
 // multiple of 128 (an even number of stages, no K tail); m and n are arbitrary.
 #include "mpgemm_kernel.hpp"
 
@@ -92,12 +93,13 @@ void sp24_kernel(SpParams sp) {
     constexpr int kRing = 3;
     constexpr int A_STAGE = KeptA::kStageBytes;     // 16 KB
     constexpr int B_STAGE = OpB::kStageBytes;       // 32 KB
-    constexpr int M_PAIR = BM * 16;                 // metadata of two stages: 16 bytes per row
+    constexpr int M_QUAD = BM * 32;                 // metadata of four stages: 32 bytes per row
     constexpr int B_BASE = kRing * A_STAGE, M_BASE = B_BASE + kRing * B_STAGE;
-    constexpr int kLoadsAB = KeptA::kSlots + OpB::kSlots;   // 12 per wave per stage (+1 metadata)
+    constexpr int kLoadsAB = KeptA::kSlots + OpB::kSlots;   // 12 per wave per stage
+    constexpr int kLoadsM = M_QUAD / 4096;                  // + 2 metadata loads every 4th stage
     static_assert(FM == 8 && FN == 8, "tile");
 
-    __shared__ __attribute__((aligned(16))) char smem_raw[M_BASE + 2 * M_PAIR];
+    __shared__ __attribute__((aligned(16))) char smem_raw[M_BASE + 2 * M_QUAD];
     lds_char *smem = (lds_char *)smem_raw;
 
     const int tid = threadIdx.x;
@@ -114,7 +116,7 @@ void sp24_kernel(SpParams sp) {
     opa.init(wave, lane, p.lda, m_left);
     opb.init(wave, lane, p.ldb, n_left, 0u);
     const int nk = p.k / 64;                         // stages (even: k is a multiple of 128)
-    const int np = nk / 2;                           // metadata pairs
+    const int nq = (nk + 3) / 4;                     // metadata quads (the last may hold two)
 
     // Stage cursors: the exact readable end of each operand bounds its last stage.
     StageCursor ca, cb, cm;
@@ -128,7 +130,7 @@ void sp24_kernel(SpParams sp) {
         const int64_t off_m = (int64_t)m0 * sp.ld_meta;
         ca.step = 64;
         cb.step = TB ? 128 : (int64_t)64 * p.ldb * 2;
-        cm.step = 16;
+        cm.step = 32;
         ca.base = (uint64_t)p.A + (uint64_t)off_a;
         cb.base = (uint64_t)p.B + (uint64_t)off_b;
         cm.base = (uint64_t)sp.meta + (uint64_t)off_m;
@@ -138,12 +140,17 @@ void sp24_kernel(SpParams sp) {
         };
         ca.last_records = last(end_a, off_a, ca.step, nk);
         cb.last_records = last(end_b, off_b, cb.step, nk);
-        cm.last_records = last(end_m, off_m, cm.step, np);
+        cm.last_records = last(end_m, off_m, cm.step, nq);
     }
-    // metadata load: lane l of wave w brings row 64 w + l (clamped to the last row)
-    const uint32_t voff_m = (uint32_t)min(64 * wave + lane, m_left - 1) * (uint32_t)sp.ld_meta;
+    // metadata load i: lane l of wave w brings bytes 16 (l % 2) .. +15 of row
+    // 128 i + 32 w + l / 2's quad (clamped to the last row) to LDS byte row * 32 + 16 (l % 2)
+    uint32_t voff_m[kLoadsM];
+#pragma unroll
+    for (int i = 0; i < kLoadsM; ++i)
+        voff_m[i] = (uint32_t)min(128 * i + 32 * wave + lane / 2, m_left - 1) * (uint32_t)sp.ld_meta +
+                    16u * (uint32_t)(lane % 2);
     // metadata read: row wm * 128 + 16 i + lane % 16, lane group g's 8 positions (2 bytes)
-    const uint32_t m_lane = (uint32_t)((wm * (BM / 2) + lane % 16) * 16 + 2 * (lane / 16));
+    const uint32_t m_lane = (uint32_t)((wm * (BM / 2) + lane % 16) * 32 + 2 * (lane / 16));
 
     f32x4 acc[FM][FN];
 #pragma unroll
@@ -153,14 +160,14 @@ void sp24_kernel(SpParams sp) {
 
     const uint32_t lds_w = (uint32_t)(uintptr_t)smem + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
     i32x4 rs_a, rs_b, rs_m;
-    // Resources of stage t (the cursors then move on); `with_meta` for even t.
+    // Resources of stage t (the cursors then move on); the metadata's for t a multiple of 4.
     auto prep = [&](int t, auto meta_c) {
         rs_a = ca.rsrc(t, nk);
         ca.advance();
         rs_b = cb.rsrc(t, nk);
         cb.advance();
         if constexpr (decltype(meta_c)::value) {
-            rs_m = cm.rsrc(t >> 1, np);
+            rs_m = cm.rsrc(t >> 2, nq);
             cm.advance();
         }
     };
@@ -168,11 +175,11 @@ void sp24_kernel(SpParams sp) {
     // stage carries it, then A's slots, then B's.
     auto load_slot = [&](int q, int mq, auto meta_c, int l) {
         constexpr bool kMeta = decltype(meta_c)::value;
-        if (kMeta && l == 0) {
-            dma16(rs_m, voff_m, 0u, lds_w + (uint32_t)(M_BASE + mq * M_PAIR));
+        if (kMeta && l < kLoadsM) {
+            dma16(rs_m, voff_m[l], 0u, lds_w + (uint32_t)(M_BASE + mq * M_QUAD + l * 4096));
             return;
         }
-        const int la = l - (kMeta ? 1 : 0);
+        const int la = l - (kMeta ? kLoadsM : 0);
         if (la < KeptA::kSlots)
             opa.load(rs_a, lds_w + (uint32_t)(q * A_STAGE), la);
         else
@@ -186,25 +193,25 @@ void sp24_kernel(SpParams sp) {
     u32x8 fb[FN - 1];
     u32x8 fb7[2];
     auto read_a = [&](int set, const lds_char *st, int i) { fa[set][i] = opa.frag(st, wm * FM + i); };
-    auto read_i = [&](int set, const lds_char *mst, int half, int i) {
-        fi[set][i] = *(const lds_u16 *)(mst + m_lane + i * 256 + 8 * half);
+    auto read_i = [&](int set, const lds_char *mst, int quarter, int i) {
+        fi[set][i] = *(const lds_u16 *)(mst + m_lane + i * 512 + 8 * quarter);
     };
     auto read_b = [&](u32x8 &dst, const lds_char *st, int j) {
         set_half(dst, 0, opb.frag(st, wn * FN + j, 0));
         set_half(dst, 1, opb.frag(st, wn * FN + j, 1));
     };
 
-    // Prologue: stages 0, 1, 2 queued (metadata pairs 0 and 1 with stages 0 and 2); wait for
-    // stage 0 and read its fragments.
+    // Prologue: stages 0, 1, 2 queued (metadata quad 0 with stage 0); wait for stage 0 and read
+    // its fragments.
     using CT = std::integral_constant<bool, true>;
     using CF = std::integral_constant<bool, false>;
     prep(0, CT{});
-    static_for<kLoadsAB + 1>([&](auto l_c) { load_slot(0, 0, CT{}, decltype(l_c)::value); });
+    static_for<kLoadsAB + kLoadsM>([&](auto l_c) { load_slot(0, 0, CT{}, decltype(l_c)::value); });
     prep(1, CF{});
     static_for<kLoadsAB>([&](auto l_c) { load_slot(1, 0, CF{}, decltype(l_c)::value); });
-    prep(2, CT{});
-    static_for<kLoadsAB + 1>([&](auto l_c) { load_slot(2, 1, CT{}, decltype(l_c)::value); });
-    wait_vmem<2 * kLoadsAB + 1>();
+    prep(2, CF{});
+    static_for<kLoadsAB>([&](auto l_c) { load_slot(2, 0, CF{}, decltype(l_c)::value); });
+    wait_vmem<2 * kLoadsAB>();
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -216,23 +223,23 @@ void sp24_kernel(SpParams sp) {
     read_b(fb7[0], smem + B_BASE, FN - 1);
     wait_lds<0>();
 
-    // Iteration s (H = s & 1) multiplies stage s (ring slot q) out of registers, reads the
-    // fragments of stage s + 1 (ring slot q + 1) and queues the loads of stage s + 3 into slot
-    // q, whose last reads were waited for at the barrier.  Its first instructions wait for
-    // stage s + 1 (at most one stage's loads, 12, may still be in flight: those of stage s + 2,
-    // which has 13 when it carries metadata, so its first load is waited for too).
-    auto iteration = [&](int s, int q, auto h_c) {
-        constexpr int H = decltype(h_c)::value;
-        constexpr bool kMeta = H == 1;               // stage s + 3 even: it carries metadata
-        constexpr int kL = kLoadsAB + (kMeta ? 1 : 0);
+    // Iteration s (S4 = s % 4, H = s & 1) multiplies stage s (ring slot q) out of registers,
+    // reads the fragments of stage s + 1 (ring slot q + 1) and queues the loads of stage s + 3
+    // into slot q, whose last reads were waited for at the barrier.  Its first instructions wait
+    // for stage s + 1 (at most one stage's loads, 12, may still be in flight: those of stage
+    // s + 2, which has 14 when it carries metadata, so its two first loads are waited for too).
+    auto iteration = [&](int s, int q, auto s4_c) {
+        constexpr int S4 = decltype(s4_c)::value, H = S4 & 1;
+        constexpr bool kMeta = S4 == 1;              // stage s + 3 a multiple of 4: metadata
+        constexpr int kL = kLoadsAB + (kMeta ? kLoadsM : 0);
         const int qn = q == kRing - 1 ? 0 : q + 1;
         wait_vmem<kLoadsAB>();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         const lds_char *stA = smem + qn * A_STAGE;
         const lds_char *stB = smem + B_BASE + qn * B_STAGE;
-        const lds_char *stM = smem + M_BASE + (((s + 1) >> 1) & 1) * M_PAIR;
-        const int mq = ((s + 3) >> 1) & 1;
+        const lds_char *stM = smem + M_BASE + (((s + 1) >> 2) & 1) * M_QUAD;
+        const int mq = ((s + 3) >> 2) & 1;
         static_for<FM * FN>([&](auto idx_c) {
             constexpr int idx = decltype(idx_c)::value;
             constexpr int j = idx / FM, i = idx % FM;   // B-block-major
@@ -243,7 +250,7 @@ void sp24_kernel(SpParams sp) {
             if constexpr (idx == 0) prep(s + 3, std::integral_constant<bool, kMeta>{});
             if constexpr (idx == 1) read_b(fb7[H ^ 1], stB, FN - 1);
             if constexpr (i == 2) read_a(H ^ 1, stA, j);
-            if constexpr (i == 3) read_i(H ^ 1, stM, (s + 1) & 1, j);
+            if constexpr (i == 3) read_i(H ^ 1, stM, (S4 + 1) & 3, j);
             if constexpr (i == FM - 1 && j < FN - 1) read_b(fb[j], stB, j);
             static_for<kL>([&](auto l_c) {
                 constexpr int l = decltype(l_c)::value;
@@ -255,12 +262,24 @@ void sp24_kernel(SpParams sp) {
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
-    int q = 0;
-    for (int s = 0; s < nk; s += 2) {
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    auto next_q = [](int x) { return x == kRing - 1 ? 0 : x + 1; };
+    int q = 0, s = 0;
+    for (; s + 4 <= nk; s += 4) {
         iteration(s, q, C0{});
-        q = q == kRing - 1 ? 0 : q + 1;
+        q = next_q(q);
         iteration(s + 1, q, C1{});
-        q = q == kRing - 1 ? 0 : q + 1;
+        q = next_q(q);
+        iteration(s + 2, q, C2{});
+        q = next_q(q);
+        iteration(s + 3, q, C3{});
+        q = next_q(q);
+    }
+    if (s < nk) {  // nk = 2 mod 4: two more stages
+        iteration(s, q, C0{});
+        q = next_q(q);
+        iteration(s + 1, q, C1{});
     }
     wait_vmem<0>();  // no direct load into LDS is left in flight when the workgroup ends
     drain_mfma(acc);
