@@ -118,9 +118,23 @@ def time_gemm(w, steps: int, warmup: int):
     ev1.record(stream)
     ev1.synchronize()
     kern_ms = ev0.elapsed_time(ev1) / steps
+    # cold caches: before each timed launch, 512 MiB written through L2 and the last-level cache
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(max(5, min(steps // 10, 30))):
+        flush.fill_(1)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        step()
+        c1.record(stream)
+        c1.synchronize()
+        cold.append(c0.elapsed_time(c1))
+    del flush
+    cold_ms = sorted(cold)[len(cold) // 2]
     tile = (256, 256) if w.sparse24 else mp.mpgemm_tile_shape(w.m, w.n, w.in_type)
     h.close()
-    return wall_ms, kern_ms, tile
+    return wall_ms, kern_ms, tile, cold_ms
 
 
 def time_bf16x3(w, steps: int, warmup: int):
@@ -216,6 +230,17 @@ def bf16x3_line(w, args) -> dict:
     return line
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_f32(w, target_s: float = 15.0):
     """The oracle's double-precision FP32 GEMM on a bounded sample of output elements."""
     import oracle
@@ -234,7 +259,7 @@ def cpu_baseline_f32(w, target_s: float = 15.0):
                     w.beta, inp.C, w.ldc, points=pts)
     t = time.perf_counter() - t0
     return {"value": 2.0 * pts[0].size * w.k / t / 1e12, "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu": cpu_model(),
             "sample": (f"{pts[0].size} output elements of the {w.m}x{w.n}x{w.k} workload, each "
                        f"a {w.k}-term FP32 dot product in double; {t:.1f} s")}
 
@@ -272,9 +297,11 @@ def cpu_baseline(w, target_s: float = 15.0):
     per_elem = t / probe[0].size
     full_s = per_elem * w.m * w.n
     if full_s <= target_s:
-        # whole passes over the m x n output, repeated to about 10 s of CPU work
-        reps = max(1, min(int(10.0 / max(full_s, 1e-3)), 50))
-        t = sum(run(None) for _ in range(reps))
+        # whole passes over the m x n output, repeated until at least 10 s of CPU work
+        reps, t = 0, 0.0
+        while (t < 10.0 and reps < 50) or reps == 0:
+            t += run(None)
+            reps += 1
         npts = reps * w.m * w.n
         what = (f"{reps} full pass(es) over the {w.m}x{w.n}x{w.k} workload's output")
     else:
@@ -287,7 +314,7 @@ def cpu_baseline(w, target_s: float = 15.0):
     if w.sparse24:
         elem += " over the kept values of a 2:4 sparse row"
     return {"value": 2.0 * npts * terms / t / 1e12, "unit": unit,
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{what}; each element a {terms}-term {elem}; {t:.1f} s"}
 
 
@@ -317,7 +344,7 @@ def main() -> int:
     if w.in_type == "f32":
         print(json.dumps(bf16x3_line(w, args)), flush=True)
         return 0
-    wall_ms, kern_ms, tile = time_gemm(w, args.steps, args.warmup)
+    wall_ms, kern_ms, tile, cold_ms = time_gemm(w, args.steps, args.warmup)
     flops = w.flops
     value = flops / (wall_ms * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -342,7 +369,9 @@ def main() -> int:
                    "in": w.in_type, "in_b": w.b_type,
                    "accumulate": "i32" if w.in_type == "i8" else "f32",
                    "out": w.out_type, "alpha": w.alpha, "beta": w.beta,
-                   "tile": f"{tile[0]}x{tile[1]}", "pct_of_peak": round(100 * value / peak, 2)},
+                   "tile": f"{tile[0]}x{tile[1]}", "pct_of_peak": round(100 * value / peak, 2),
+                   "cold_cache_kernel_ms": round(cold_ms, 5),
+                   "cold_cache_TFLOPs": round(flops / (cold_ms * 1e-3) / 1e12, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic},
@@ -359,7 +388,7 @@ def main() -> int:
         line["cpu_baseline"] = cpu_baseline(w)
     if args.all:
         for name, wx in WORKLOADS.items():
-            wm, km, tl = time_gemm(wx, max(10, args.steps // 2), args.warmup)
+            wm, km, tl, _ = time_gemm(wx, max(10, args.steps // 2), args.warmup)
             pk = PEAK_TFLOPS[wx.in_type]
             rec = {"workload": name, "kernel_ms": round(km, 5), "wall_ms": round(wm, 5),
                    "tflops_kernel": round(wx.flops / km / 1e9, 2),
