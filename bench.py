@@ -10,6 +10,7 @@ on a bounded sample of the same workload.
   python bench.py --workload f32_4096_nt_bf16x3   # FP32 GEMM as three BF16 products
   python bench.py --workload e4m3_4096_nt         # FP8 E4M3 inputs
   python bench.py --workload f16_sp24_4096_nt     # 2:4 structured-sparse FP16 A
+  python bench.py --workload i8_sp24_4096_nn      # 2:4 structured-sparse INT8 A
   python bench.py --copy-calibration   # a plain copy of known size, for counter scaling
 """
 from __future__ import annotations
@@ -94,7 +95,7 @@ def time_gemm(w, steps: int, warmup: int):
         if w.sparse24:
             mp.mpgemm_run_sp24(h.h, w.transb, w.m, w.n, w.k, alpha, dA, w.in_type, w.lda, dM,
                                w.ld_meta, dB, w.b_type, w.ldb, beta, dC, w.out_type, w.ldc, dD,
-                               stream=stream)
+                               compute, stream=stream)
         else:
             mp.mpgemm_run(h.h, w.transa, w.transb, w.m, w.n, w.k, alpha, dA, w.in_type, w.lda,
                           dB, w.b_type, w.ldb, beta, dC, w.out_type, w.ldc, dD, compute,
@@ -277,7 +278,10 @@ def cpu_baseline(w, target_s: float = 15.0):
 
     def run(pts):
         t0 = time.perf_counter()
-        if w.sparse24:
+        if w.sparse24 and w.in_type == "i8":
+            oracle.gemm_sp24_int(w.transb, w.m, w.n, w.k, int(w.alpha), inp.A, w.lda, inp.meta,
+                                 w.ld_meta, inp.B, w.ldb, int(w.beta), inp.C, w.ldc, points=pts)
+        elif w.sparse24:
             oracle.gemm_sp24(w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda, inp.meta,
                              w.ld_meta, inp.B, w.ldb, w.beta, inp.C, w.out_type, w.ldc,
                              points=pts)
@@ -379,10 +383,10 @@ def main() -> int:
     if w.sparse24:
         # the work is the kept products (2 m n k/2); the dense GEMM of the same shape would be
         # twice that
-        line["metric"] = ("TFLOP/s of the kept products (2 m n k/2) of a 2:4 sparse A, and % "
+        line["metric"] = (f"{unit} of the kept products (2 m n k/2) of a 2:4 sparse A, and % "
                           "of MI355X dense MFMA peak at 1 GPU")
         line["config"]["sparsity"] = "2:4 on A (kept values m x k/2 plus 2-bit positions)"
-        line["config"]["dense_equivalent_TFLOPs"] = round(2 * value, 2)
+        line["config"]["dense_equivalent_" + unit.replace("/", "")] = round(2 * value, 2)
         line["config"]["transa"] = "N"
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)

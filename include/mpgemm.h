@@ -182,11 +182,14 @@ mpgemm_status_t mpgemm_run_bf16x3(mpgemm_handle_t handle, mpgemm_op_t transa,
  *           the same row of op(B).
  *   B, C, D, transb, ldb, ldc, alpha, beta: as for mpgemm_run; A is never transposed.
  *   Types:  a_type = b_type = MPGEMM_R_16F or MPGEMM_R_16BF, compute MPGEMM_R_32F, c_type
- *           MPGEMM_R_32F or a_type.  Numerics as for the dense FP16/BF16 GEMM, over the k/2
- *           kept products.
+ *           MPGEMM_R_32F or a_type: numerics as for the dense FP16/BF16 GEMM, over the k/2
+ *           kept products (blocks of 8 kept products, in kept order); or a_type = b_type =
+ *           MPGEMM_R_8I with compute and c_type MPGEMM_R_32I: exact, wrapping INT32 arithmetic
+ *           as for the dense INT8 GEMM (alpha and beta point to int32_t).
  *   Sizes:  k a multiple of 128 (else MPGEMM_STATUS_NOT_SUPPORTED); m, n arbitrary.
- *   Alignment: Ac, meta, B, C (when read), D 16-byte aligned; lda and ldb multiples of 8,
- *           ld_meta of 16 bytes, ldc as for mpgemm_run.
+ *   Alignment: Ac, meta, B, C (when read), D 16-byte aligned; rows of Ac and B (lda, ldb
+ *           elements) and of the metadata (ld_meta bytes) multiples of 16 bytes, ldc as for
+ *           mpgemm_run.
  * Ownership, ordering and errors as for mpgemm_run; nothing is allocated. */
 mpgemm_status_t mpgemm_run_sp24(mpgemm_handle_t handle, mpgemm_op_t transb, int64_t m, int64_t n,
                                 int64_t k, const void *alpha, const void *Ac,

@@ -161,12 +161,14 @@ def mpgemm_run_bf16x3(handle, transa, transb, m, n, k, alpha, A, lda, B, ldb, be
 def mpgemm_run_sp24(handle, transb, m, n, k, alpha, Ac, a_type, lda, meta, ld_meta, B, b_type,
                     ldb, beta, C, c_type, ldc, D, compute_type="f32", stream=None,
                     check: bool = True) -> int:
-    """Queue the GEMM with a 2:4 structured-sparse A given as kept values Ac and metadata."""
-    al, be = ctypes.c_float(float(alpha)), ctypes.c_float(float(beta))
+    """Queue the GEMM with a 2:4 structured-sparse A given as kept values Ac and metadata
+    (alpha and beta are float for F32 compute, int for I32)."""
+    ct = _dtype(compute_type)
+    al, be = _scalar(alpha, ct), _scalar(beta, ct)
     st = load().mpgemm_run_sp24(handle, _op(transb), m, n, k, ctypes.byref(al), _ptr(Ac),
                                 _dtype(a_type), lda, _ptr(meta), ld_meta, _ptr(B), _dtype(b_type),
                                 ldb, ctypes.byref(be), _ptr(C), _dtype(c_type), ldc, _ptr(D),
-                                _dtype(compute_type), _stream(stream))
+                                ct, _stream(stream))
     if check and st != SUCCESS:
         raise MpgemmError(st, "mpgemm_run_sp24")
     return st
@@ -175,11 +177,12 @@ def mpgemm_run_sp24(handle, transb, m, n, k, alpha, Ac, a_type, lda, meta, ld_me
 def mpgemm_check_sp24(transb, m, n, k, alpha, Ac, a_type, lda, meta, ld_meta, B, b_type, ldb,
                       beta, C, c_type, ldc, D, compute_type="f32") -> int:
     """Host-only argument check of mpgemm_run_sp24."""
-    al, be = ctypes.c_float(float(alpha)), ctypes.c_float(float(beta))
+    ct = _dtype(compute_type)
+    al, be = _scalar(alpha, ct), _scalar(beta, ct)
     return load().mpgemm_check_sp24(_op(transb), m, n, k, ctypes.byref(al), _ptr(Ac),
                                     _dtype(a_type), lda, _ptr(meta), ld_meta, _ptr(B),
                                     _dtype(b_type), ldb, ctypes.byref(be), _ptr(C), _dtype(c_type),
-                                    ldc, _ptr(D), _dtype(compute_type))
+                                    ldc, _ptr(D), ct)
 
 
 def mpgemm_bf16x3_workspace_size(transa, transb, m: int, n: int, k: int) -> int:

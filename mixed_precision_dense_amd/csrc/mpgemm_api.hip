@@ -343,9 +343,16 @@ mpgemm_status_t mpgemm_check_sp24(mpgemm_op_t transb, int64_t m, int64_t n, int6
     if (!valid_dtype(a_type) || !valid_dtype(b_type) || !valid_dtype(c_type) ||
         !valid_dtype(compute_type))
         return MPGEMM_STATUS_NOT_SUPPORTED;
-    if (a_type != b_type || (a_type != MPGEMM_R_16F && a_type != MPGEMM_R_16BF) ||
-        compute_type != MPGEMM_R_32F || (c_type != MPGEMM_R_32F && c_type != a_type))
+    if (a_type != b_type) return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (a_type == MPGEMM_R_8I) {
+        if (compute_type != MPGEMM_R_32I || c_type != MPGEMM_R_32I) return MPGEMM_STATUS_NOT_SUPPORTED;
+    } else if (a_type == MPGEMM_R_16F || a_type == MPGEMM_R_16BF) {
+        if (compute_type != MPGEMM_R_32F || (c_type != MPGEMM_R_32F && c_type != a_type))
+            return MPGEMM_STATUS_NOT_SUPPORTED;
+    } else {
         return MPGEMM_STATUS_NOT_SUPPORTED;
+    }
+    const int ea = elem_bytes(a_type);
     if (k % 128) return MPGEMM_STATUS_NOT_SUPPORTED;
     const bool tb = transb == MPGEMM_OP_T;
     const int64_t min_ldb = tb ? k : n;
@@ -359,10 +366,10 @@ mpgemm_status_t mpgemm_check_sp24(mpgemm_op_t transb, int64_t m, int64_t n, int6
     const int ec = elem_bytes(c_type);
     if (!aligned16(D) || (read_c && !aligned16(C))) return MPGEMM_STATUS_NOT_SUPPORTED;
     if (k > 0 && (!aligned16(Ac) || !aligned16(meta) || !aligned16(B))) return MPGEMM_STATUS_NOT_SUPPORTED;
-    if ((lda * 2) % 16 || (ldb * 2) % 16 || ld_meta % 16 || (ldc * ec) % 16)
+    if ((lda * ea) % 16 || (ldb * ea) % 16 || ld_meta % 16 || (ldc * ec) % 16)
         return MPGEMM_STATUS_NOT_SUPPORTED;
     const int64_t limit = ((int64_t)1 << 31) - 4096;
-    if (256 * lda * 2 > limit || 256 * ldb * 2 > limit || 256 * ld_meta > limit ||
+    if (256 * lda * ea > limit || 256 * ldb * ea > limit || 256 * ld_meta > limit ||
         256 * ldc * ec > limit)
         return MPGEMM_STATUS_NOT_SUPPORTED;
     return MPGEMM_STATUS_SUCCESS;
@@ -397,16 +404,24 @@ mpgemm_status_t mpgemm_run_sp24(mpgemm_handle_t handle, mpgemm_op_t transb, int6
     p.k = (int)k;
     p.read_c = beta_is_zero(beta, compute_type) ? 0 : 1;
     p.C = p.read_c ? C : nullptr;
-    memcpy(&p.alpha_f, alpha, sizeof(float));
-    memcpy(&p.beta_f, beta, sizeof(float));
+    p.alpha_f = p.beta_f = 0.0f;
     p.alpha_i = p.beta_i = 0;
+    if (compute_type == MPGEMM_R_32I) {
+        memcpy(&p.alpha_i, alpha, sizeof(int32_t));
+        memcpy(&p.beta_i, beta, sizeof(int32_t));
+    } else {
+        memcpy(&p.alpha_f, alpha, sizeof(float));
+        memcpy(&p.beta_f, beta, sizeof(float));
+    }
     p.tiles_m = (int)((m + mpg::kSpTileM - 1) / mpg::kSpTileM);
     p.tiles_n = (int)((n + mpg::kSpTileN - 1) / mpg::kSpTileN);
     sp.meta = meta;
     sp.ld_meta = ld_meta;
-    const int in = a_type == MPGEMM_R_16F ? mpg::IN_F16 : mpg::IN_BF16;
-    const int out = c_type == MPGEMM_R_32F ? mpg::OUT_F32
-                                          : (a_type == MPGEMM_R_16F ? mpg::OUT_F16 : mpg::OUT_BF16);
+    const int in = a_type == MPGEMM_R_8I ? mpg::IN_I8
+                                         : (a_type == MPGEMM_R_16F ? mpg::IN_F16 : mpg::IN_BF16);
+    const int out = c_type == MPGEMM_R_32I ? mpg::OUT_I32
+                    : c_type == MPGEMM_R_32F ? mpg::OUT_F32
+                    : (a_type == MPGEMM_R_16F ? mpg::OUT_F16 : mpg::OUT_BF16);
     const hipError_t e = mpg::launch_sp24(in, out, transb == MPGEMM_OP_T, sp, (hipStream_t)stream);
     return e == hipSuccess ? MPGEMM_STATUS_SUCCESS : MPGEMM_STATUS_LAUNCH_FAILED;
 }

@@ -6,19 +6,21 @@
 // Sparse tensor cores as the page "稀疏张量核心加速模板计算的技术解析" (sparse tensor cores
 // for stencil computation) describes them in sections 1.2.1 and 1.3.2: a 2:4 sparse operand is
 // held as its kept values (half of k) plus 2 bits of metadata per kept value (its position
-// within its group of 4), and the matrix instruction skips the zeros.  Here the instruction is
-// v_smfmac_f32_16x16x64_{f16,bf16}: a 16 x 16 output block over 64 logical k from A's kept
-// values (lane group g: the 8 kept values of k 16 g .. 16 g + 15, 16 bytes), B's 64 k-rows (two
-// 32-k fragments of the dense layout, 32 bytes) and a 16-bit index (2 bits per kept value, low
-// half of the register) -- lane layouts measured on gfx950.
+// within its group of 4), and the matrix instruction skips the zeros.  Here the instructions
+// are v_smfmac_f32_16x16x64_{f16,bf16} and v_smfmac_i32_16x16x128_i8: a 16 x 16 output block
+// over one k step (64 logical k for 16-bit inputs, 128 for INT8) from A's kept values (lane
+// group g: the 16 bytes of kept values of logical k 16 g .. 16 g + 15, resp. 32 g .. 32 g + 31),
+// B's k-rows (the two dense fragments of the step's halves, 32 bytes) and an index register
+// (2 bits per kept value, in k order: the low 16 bits for 16-bit inputs, all 32 for INT8) --
+// lane layouts measured on gfx950.
 //
 // One sparse instruction does the useful work of one dense 16 x 16 x 32 in the same issue
 // time, so per MFMA cycle the sparse loop needs about twice the bytes of the dense kernel.  The
 // loop is therefore built around the global -> LDS stream:
 //   * tile 256 x 256 (2 x 2 waves of 128 x 128), the largest the accumulators allow;
-//   * a stage is one sparse k step of 64 logical k: A's 32 kept values per row (64 bytes),
-//     B's 64 k-rows (the dense kernel's 16-bit B stage) -- 48 KB -- plus, every fourth stage,
-//     32 metadata bytes per row covering four stages (8 KB; two lanes per row, so one 32-byte
+//   * a stage is one sparse k step: A's kept values, 64 bytes per row, and B's k-rows (the
+//     dense kernel's B stage) -- 48 KB -- plus, every fourth (16-bit) or second (INT8) stage,
+//     32 metadata bytes per row covering those stages (8 KB; two lanes per row, so one 32-byte
 //     request per row: the loop is bound by the L2 request rate, not by bytes);
 //   * an LDS ring of three stages (and two metadata quads), so that two stages of loads are in
 //     flight while the third is multiplied: each iteration waits only for the older one;
@@ -26,7 +28,7 @@
 //     is refilled right after its last MFMA, and B block 7 alternates between two registers so
 //     that its refill is not the last instruction of the iteration.
 // LDS: [A ring 3 x 16 KB | B ring 3 x 32 KB | metadata 2 x 8 KB] = 160 KB.  k must be a
-// multiple of 128 (an even number of stages, no K tail); m and n are arbitrary.
+// multiple of 128 (whole stages, no K tail); m and n are arbitrary.
 #include "mpgemm_kernel.hpp"
 
 namespace mpg {
@@ -44,8 +46,14 @@ template <> struct SMma<IN_BF16> {
         asm("v_smfmac_f32_16x16x64_bf16 %0, %1, %2, %3" : "+a"(c) : "v"(a), "v"(b), "v"(idx));
     }
 };
+template <> struct SMma<IN_I8> {
+    static __device__ __forceinline__ void run(u32x4 a, u32x8 b, uint32_t idx, i32x4 &c) {
+        asm("v_smfmac_i32_16x16x128_i8 %0, %1, %2, %3" : "+a"(c) : "v"(a), "v"(b), "v"(idx));
+    }
+};
 
 typedef __attribute__((address_space(3))) unsigned short lds_u16;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 // A's kept values, K-contiguous: a stage holds 256 rows of 64 bytes (row r at r * 64, its
@@ -61,8 +69,8 @@ struct KeptA {
     static __device__ __forceinline__ int swz(int r) { return ((r >> 3) & 1) << 1; }
     // Load slot i of wave w, lane l fills LDS bytes i * 4096 + w * 1024 + l * 16 of the stage:
     // row 64 i + 16 w + l / 4, physical chunk l % 4.  Rows past the matrix repeat its last row.
-    __device__ __forceinline__ void init(int wave, int lane, int64_t lda, int m_left) {
-        const uint32_t row_bytes = (uint32_t)(lda * 2);
+    __device__ __forceinline__ void init(int wave, int lane, int64_t lda_bytes, int m_left) {
+        const uint32_t row_bytes = (uint32_t)lda_bytes;
 #pragma unroll
         for (int i = 0; i < kSlots; ++i) {
             const int r = 64 * i + 16 * wave + lane / 4;
@@ -89,7 +97,13 @@ void sp24_kernel(SpParams sp) {
     const Params &p = sp.p;
     constexpr int BM = kSpTileM, BN = kSpTileN;
     constexpr int FM = BM / 32, FN = BN / 32;       // 16-wide blocks per wave (2 x 2 waves)
-    using OpB = Operand<2, TB, BN / 32>;            // 64 k-rows of B per stage
+    constexpr bool kInt = IN == IN_I8;
+    constexpr int EB = kInt ? 1 : 2;                // bytes per element
+    using OpB = Operand<EB, TB, BN / 32>;           // one stage of B: 64 (16-bit) or 128 k-rows
+    using acc_t = typename MmaAcc<IN>::type;
+    constexpr int kStageK = 128 / EB;               // logical k per stage: 64 kept bytes per row
+    constexpr int kMetaStages = kInt ? 2 : 4;       // stages per 32-byte metadata row
+    static_assert(OpB::kStageK == kStageK, "A and B stages cover the same k");
     constexpr int kRing = 3;
     constexpr int A_STAGE = KeptA::kStageBytes;     // 16 KB
     constexpr int B_STAGE = OpB::kStageBytes;       // 32 KB
@@ -113,23 +127,23 @@ void sp24_kernel(SpParams sp) {
 
     KeptA opa;
     OpB opb;
-    opa.init(wave, lane, p.lda, m_left);
+    opa.init(wave, lane, p.lda * EB, m_left);
     opb.init(wave, lane, p.ldb, n_left, 0u);
-    const int nk = p.k / 64;                         // stages (even: k is a multiple of 128)
-    const int nq = (nk + 3) / 4;                     // metadata quads (the last may hold two)
+    const int nk = p.k / kStageK;                    // stages (k is a multiple of 128)
+    const int nq = (nk + kMetaStages - 1) / kMetaStages;   // 32-byte metadata groups
 
     // Stage cursors: the exact readable end of each operand bounds its last stage.
     StageCursor ca, cb, cm;
     {
-        const int64_t end_a = (int64_t)(p.m - 1) * p.lda * 2 + (int64_t)p.k;   // k/2 kept x 2 B
+        const int64_t end_a = (int64_t)(p.m - 1) * p.lda * EB + (int64_t)p.k / 2 * EB;
         const int64_t rb = TB ? p.n : p.k, clb = TB ? p.k : p.n;
-        const int64_t end_b = (rb - 1) * p.ldb * 2 + ((clb * 2 + 15) & ~(int64_t)15);
+        const int64_t end_b = (rb - 1) * p.ldb * EB + ((clb * EB + 15) & ~(int64_t)15);
         const int64_t end_m = (int64_t)(p.m - 1) * sp.ld_meta + (int64_t)p.k / 8;
-        const int64_t off_a = (int64_t)m0 * p.lda * 2;
-        const int64_t off_b = TB ? (int64_t)n0 * p.ldb * 2 : (int64_t)n0 * 2;
+        const int64_t off_a = (int64_t)m0 * p.lda * EB;
+        const int64_t off_b = TB ? (int64_t)n0 * p.ldb * EB : (int64_t)n0 * EB;
         const int64_t off_m = (int64_t)m0 * sp.ld_meta;
         ca.step = 64;
-        cb.step = TB ? 128 : (int64_t)64 * p.ldb * 2;
+        cb.step = TB ? 128 : (int64_t)kStageK * p.ldb * EB;
         cm.step = 32;
         ca.base = (uint64_t)p.A + (uint64_t)off_a;
         cb.base = (uint64_t)p.B + (uint64_t)off_b;
@@ -149,25 +163,28 @@ void sp24_kernel(SpParams sp) {
     for (int i = 0; i < kLoadsM; ++i)
         voff_m[i] = (uint32_t)min(128 * i + 32 * wave + lane / 2, m_left - 1) * (uint32_t)sp.ld_meta +
                     16u * (uint32_t)(lane % 2);
-    // metadata read: row wm * 128 + 16 i + lane % 16, lane group g's 8 positions (2 bytes)
-    const uint32_t m_lane = (uint32_t)((wm * (BM / 2) + lane % 16) * 32 + 2 * (lane / 16));
+    // metadata read: row wm * 128 + 16 i + lane % 16, lane group g's 8 (16-bit) or 16 (INT8)
+    // positions: 2 or 4 bytes
+    constexpr int kIdxBytes = kInt ? 4 : 2;
+    const uint32_t m_lane = (uint32_t)((wm * (BM / 2) + lane % 16) * 32 + kIdxBytes * (lane / 16));
 
-    f32x4 acc[FM][FN];
+    acc_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{};
+        for (int j = 0; j < FN; ++j) acc[i][j] = acc_t{};
 
     const uint32_t lds_w = (uint32_t)(uintptr_t)smem + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
     i32x4 rs_a, rs_b, rs_m;
-    // Resources of stage t (the cursors then move on); the metadata's for t a multiple of 4.
+    // Resources of stage t (the cursors then move on); the metadata's for t a multiple of
+    // kMetaStages.
     auto prep = [&](int t, auto meta_c) {
         rs_a = ca.rsrc(t, nk);
         ca.advance();
         rs_b = cb.rsrc(t, nk);
         cb.advance();
         if constexpr (decltype(meta_c)::value) {
-            rs_m = cm.rsrc(t >> 2, nq);
+            rs_m = cm.rsrc(t / kMetaStages, nq);
             cm.advance();
         }
     };
@@ -193,25 +210,31 @@ void sp24_kernel(SpParams sp) {
     u32x8 fb[FN - 1];
     u32x8 fb7[2];
     auto read_a = [&](int set, const lds_char *st, int i) { fa[set][i] = opa.frag(st, wm * FM + i); };
-    auto read_i = [&](int set, const lds_char *mst, int quarter, int i) {
-        fi[set][i] = *(const lds_u16 *)(mst + m_lane + i * 512 + 8 * quarter);
+    // positions of stage part `part` (the stage's index within its metadata group)
+    auto read_i = [&](int set, const lds_char *mst, int part, int i) {
+        if constexpr (kInt)
+            fi[set][i] = *(const lds_u32 *)(mst + m_lane + i * 512 + 16 * part);
+        else
+            fi[set][i] = *(const lds_u16 *)(mst + m_lane + i * 512 + 8 * part);
     };
     auto read_b = [&](u32x8 &dst, const lds_char *st, int j) {
         set_half(dst, 0, opb.frag(st, wn * FN + j, 0));
         set_half(dst, 1, opb.frag(st, wn * FN + j, 1));
     };
 
-    // Prologue: stages 0, 1, 2 queued (metadata quad 0 with stage 0); wait for stage 0 and read
-    // its fragments.
+    // Prologue: stages 0, 1, 2 queued (metadata group 0 with stage 0, group 1 with stage 2
+    // when groups are pairs); wait for stage 0 and read its fragments.
     using CT = std::integral_constant<bool, true>;
     using CF = std::integral_constant<bool, false>;
+    using CM2 = std::integral_constant<bool, kMetaStages == 2>;
+    constexpr int kLoads2 = kLoadsAB + (kMetaStages == 2 ? kLoadsM : 0);
     prep(0, CT{});
     static_for<kLoadsAB + kLoadsM>([&](auto l_c) { load_slot(0, 0, CT{}, decltype(l_c)::value); });
     prep(1, CF{});
     static_for<kLoadsAB>([&](auto l_c) { load_slot(1, 0, CF{}, decltype(l_c)::value); });
-    prep(2, CF{});
-    static_for<kLoadsAB>([&](auto l_c) { load_slot(2, 0, CF{}, decltype(l_c)::value); });
-    wait_vmem<2 * kLoadsAB>();
+    prep(2, CM2{});
+    static_for<kLoads2>([&](auto l_c) { load_slot(2, 1, CM2{}, decltype(l_c)::value); });
+    wait_vmem<kLoadsAB + kLoads2>();
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -230,7 +253,7 @@ void sp24_kernel(SpParams sp) {
     // s + 2, which has 14 when it carries metadata, so its two first loads are waited for too).
     auto iteration = [&](int s, int q, auto s4_c) {
         constexpr int S4 = decltype(s4_c)::value, H = S4 & 1;
-        constexpr bool kMeta = S4 == 1;              // stage s + 3 a multiple of 4: metadata
+        constexpr bool kMeta = (S4 + 3) % kMetaStages == 0;   // stage s + 3 starts a group
         constexpr int kL = kLoadsAB + (kMeta ? kLoadsM : 0);
         const int qn = q == kRing - 1 ? 0 : q + 1;
         wait_vmem<kLoadsAB>();
@@ -238,8 +261,8 @@ void sp24_kernel(SpParams sp) {
         __builtin_amdgcn_sched_barrier(0);
         const lds_char *stA = smem + qn * A_STAGE;
         const lds_char *stB = smem + B_BASE + qn * B_STAGE;
-        const lds_char *stM = smem + M_BASE + (((s + 1) >> 2) & 1) * M_QUAD;
-        const int mq = ((s + 3) >> 2) & 1;
+        const lds_char *stM = smem + M_BASE + (((s + 1) / kMetaStages) & 1) * M_QUAD;
+        const int mq = ((s + 3) / kMetaStages) & 1;
         static_for<FM * FN>([&](auto idx_c) {
             constexpr int idx = decltype(idx_c)::value;
             constexpr int j = idx / FM, i = idx % FM;   // B-block-major
@@ -250,7 +273,7 @@ void sp24_kernel(SpParams sp) {
             if constexpr (idx == 0) prep(s + 3, std::integral_constant<bool, kMeta>{});
             if constexpr (idx == 1) read_b(fb7[H ^ 1], stB, FN - 1);
             if constexpr (i == 2) read_a(H ^ 1, stA, j);
-            if constexpr (i == 3) read_i(H ^ 1, stM, (S4 + 1) & 3, j);
+            if constexpr (i == 3) read_i(H ^ 1, stM, (S4 + 1) % kMetaStages, j);
             if constexpr (i == FM - 1 && j < FN - 1) read_b(fb[j], stB, j);
             static_for<kL>([&](auto l_c) {
                 constexpr int l = decltype(l_c)::value;
@@ -276,14 +299,22 @@ void sp24_kernel(SpParams sp) {
         iteration(s + 3, q, C3{});
         q = next_q(q);
     }
-    if (s < nk) {  // nk = 2 mod 4: two more stages
+    // The remaining 1-3 stages, in pairs: a stage past K reads zero records for all its
+    // operands, so it multiplies zeros into the accumulators, which leaves them unchanged.
+    if (s < nk) {
         iteration(s, q, C0{});
         q = next_q(q);
         iteration(s + 1, q, C1{});
+        q = next_q(q);
+        if (s + 2 < nk) {
+            iteration(s + 2, q, C2{});
+            q = next_q(q);
+            iteration(s + 3, q, C3{});
+        }
     }
     wait_vmem<0>();  // no direct load into LDS is left in flight when the workgroup ends
     drain_mfma(acc);
-    store_tile<false, OUT, FM, FN, BM, BN>(p, acc, m0, n0, wm, wn, lane, full_mn, m_left, n_left);
+    store_tile<kInt, OUT, FM, FN, BM, BN>(p, acc, m0, n0, wm, wn, lane, full_mn, m_left, n_left);
 }
 
 template __global__ void sp24_kernel<IN_F16, OUT_F32, false>(SpParams);
@@ -294,6 +325,8 @@ template __global__ void sp24_kernel<IN_BF16, OUT_F32, false>(SpParams);
 template __global__ void sp24_kernel<IN_BF16, OUT_F32, true>(SpParams);
 template __global__ void sp24_kernel<IN_BF16, OUT_BF16, false>(SpParams);
 template __global__ void sp24_kernel<IN_BF16, OUT_BF16, true>(SpParams);
+template __global__ void sp24_kernel<IN_I8, OUT_I32, false>(SpParams);
+template __global__ void sp24_kernel<IN_I8, OUT_I32, true>(SpParams);
 
 namespace {
 template <int IN, int OUT, bool TB>
@@ -313,6 +346,7 @@ hipError_t launch_sp24(int in, int out, bool tb, const SpParams &sp, hipStream_t
     if (in == IN_F16 && out == OUT_F16) return by_layout<IN_F16, OUT_F16>(tb, sp, s);
     if (in == IN_BF16 && out == OUT_F32) return by_layout<IN_BF16, OUT_F32>(tb, sp, s);
     if (in == IN_BF16 && out == OUT_BF16) return by_layout<IN_BF16, OUT_BF16>(tb, sp, s);
+    if (in == IN_I8 && out == OUT_I32) return by_layout<IN_I8, OUT_I32>(tb, sp, s);
     return hipErrorInvalidValue;
 }
 

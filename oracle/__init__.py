@@ -109,6 +109,9 @@ def _load() -> ctypes.CDLL:
         lib.oracle_gemm_sp24_mfma_points.argtypes = [i32, i64, flt, vp, i32, i64, vp, i64, vp, i64,
                                                      flt, vp, i32, i64, i32, i32, i32, i32, i64,
                                                      vp, vp, vp]
+        lib.oracle_gemm_sp24_int_points.restype = i32
+        lib.oracle_gemm_sp24_int_points.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64, i64,
+                                                    vp, i64, i64, vp, vp, vp]
         lib.oracle_num_threads.restype = i32
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -422,6 +425,33 @@ def gemm_sp24(transb: bool, m: int, n: int, k: int, alpha: float, Ac: np.ndarray
     if points is None:
         v, S, bc = v.reshape(m, n), S.reshape(m, n), bc.reshape(m, n)
     return FpReference(v, S, bc)
+
+
+def gemm_sp24_int(transb: bool, m: int, n: int, k: int, alpha: int, Ac: np.ndarray, lda: int,
+                  meta: np.ndarray, ld_meta: int, B: np.ndarray, ldb: int, beta: int,
+                  C: Optional[np.ndarray], ldc: int, points: Optional[tuple] = None) -> np.ndarray:
+    """INT8 2:4 sparse A -> INT32, exact, wrapping modulo 2^32 (mpgemm_oracle.c,
+    oracle_gemm_sp24_int_points).  Returns int32 values (m x n, or at the points)."""
+    _check_storage("A", Ac, "i8")
+    _check_storage("B", B, "i8")
+    if beta != 0:
+        _check_storage("C", C, "i32")
+    else:
+        C = None
+    meta = np.ascontiguousarray(meta, dtype=np.uint8)
+    if points is None:
+        ii, jj = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+        ii, jj = ii.reshape(-1), jj.reshape(-1)
+    else:
+        ii, jj = points
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    d = np.empty(ii.shape, np.int32)
+    _load().oracle_gemm_sp24_int_points(int(bool(transb)), k, int(alpha), _ptr(Ac), lda,
+                                        meta.ctypes.data, ld_meta, _ptr(B), ldb, int(beta),
+                                        _ptr(C), ldc, ii.size, ii.ctypes.data, jj.ctypes.data,
+                                        d.ctypes.data)
+    return d.reshape(m, n) if points is None else d
 
 
 # Kept products per block of the sparse matrix cores (v_smfmac 16x16x64 FP16/BF16): eight, i.e.

@@ -877,3 +877,27 @@ int oracle_gemm_sp24_mfma_points(int transb, int64_t k, float alpha, const void 
     }
     return failed ? -2 : 0;
 }
+
+/* INT8 2:4 sparse A: D(i, c) = alpha * sum_j Ac(i, j) * B(4 (j / 2) + idx(i, j), c)
+ * + beta * C(i, c), exact in int64, then wrapped modulo 2^32 like the dense INT8 oracle. */
+int oracle_gemm_sp24_int_points(int transb, int64_t k, int64_t alpha, const int8_t *Ac,
+                                int64_t lda, const uint8_t *meta, int64_t ld_meta,
+                                const int8_t *B, int64_t ldb, int64_t beta, const int32_t *C,
+                                int64_t ldc, int64_t npts, const int64_t *ii, const int64_t *jj,
+                                int32_t *d)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < npts; ++t) {
+        const int64_t i = ii[t], c = jj[t];
+        int64_t s = 0;
+        for (int64_t j = 0; j < k / 2; ++j) {
+            const int idx = (meta[i * ld_meta + j / 4] >> (2 * (j % 4))) & 3;
+            s += (int64_t)Ac[i * lda + j] * (int64_t)B[b_index(transb, ldb, 4 * (j / 2) + idx, c)];
+        }
+        uint64_t out = (uint64_t)alpha * (uint64_t)s;
+        if (beta != 0)
+            out += (uint64_t)beta * (uint64_t)(int64_t)C[i * ldc + c];
+        d[t] = (int32_t)(uint32_t)out;
+    }
+    return 0;
+}

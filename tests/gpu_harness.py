@@ -194,9 +194,10 @@ def run_sp24(inp: Inputs, in_place: bool = False, check: bool = True):
     else:
         dC = mp.device_buffer(inp.C, w.out_type) if inp.C is not None else None
         dD = torch.full((d_bytes,), SENTINEL, dtype=torch.uint8, device="cuda")
+    compute = "i32" if w.in_type == "i8" else "f32"
     st = mp.mpgemm_run_sp24(handle().h, w.transb, w.m, w.n, w.k, w.alpha, dA, w.in_type, w.lda,
                             dM, w.ld_meta, dB, w.in_type, w.ldb, w.beta, dC, w.out_type, w.ldc,
-                            dD, check=check)
+                            dD, compute, check=check)
     torch.cuda.synchronize()
     raw = dD.cpu().numpy()
     D = raw[: w.m * w.ldc * ob].view(np.uint8)
@@ -207,12 +208,16 @@ def run_sp24(inp: Inputs, in_place: bool = False, check: bool = True):
             guard_ok &= bool(np.array_equal(pad, inp.C.view(np.uint8).reshape(w.m, w.ldc * ob)[:, w.n * ob:]))
         else:
             guard_ok &= bool(np.all(pad == SENTINEL))
-    storage = {"f16": np.uint16, "bf16": np.uint16, "f32": np.float32}[w.out_type]
+    storage = {"f16": np.uint16, "bf16": np.uint16, "f32": np.float32, "i32": np.int32}[w.out_type]
     return GpuResult(D=D.view(storage).reshape(w.m, w.ldc), guard_ok=guard_ok), st
 
 
 def sp24_ref(inp: Inputs, points=None):
     w = inp.w
+    if w.in_type == "i8":
+        return oracle.gemm_sp24_int(w.transb, w.m, w.n, w.k, int(w.alpha), inp.A, w.lda,
+                                    inp.meta, w.ld_meta, inp.B, w.ldb, int(w.beta), inp.C, w.ldc,
+                                    points=points)
     return oracle.gemm_sp24(w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda, inp.meta,
                             w.ld_meta, inp.B, w.ldb, w.beta, inp.C, w.out_type, w.ldc,
                             points=points)
@@ -224,6 +229,8 @@ def compare_sp24(inp: Inputs, res: GpuResult, exact: bool = False, points=None):
     D = res.D[:, : w.n]
     if points is not None:
         D = D[points[0], points[1]]
+    if w.in_type == "i8":
+        return oracle.check_int(np.ascontiguousarray(D), sp24_ref(inp, points))
     return oracle.check_fp(np.ascontiguousarray(D), w.out_type, sp24_ref(inp, points),
                            max(w.k // 2, 1), w.alpha, exact=exact)
 

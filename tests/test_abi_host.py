@@ -196,7 +196,17 @@ def test_sp24_contract():
     # types outside the matrix
     assert chk_sp(a_type="f16", b_type="bf16") == ST["NOT_SUPPORTED"]
     assert chk_sp(c_type="bf16") == ST["NOT_SUPPORTED"]
-    assert chk_sp(a_type="i8", b_type="i8", c_type="i32", compute_type="i32") == ST["NOT_SUPPORTED"]
+    assert chk_sp(a_type="i8", b_type="i8", c_type="i32", compute_type="i32", alpha=2,
+                  beta=0) == ST["SUCCESS"]
+    assert chk_sp(a_type="i8", b_type="i8", c_type="i32", compute_type="i32", lda=144,
+                  ldb=272) == ST["SUCCESS"]                 # 16-byte rows of 1-byte elements
+    assert chk_sp(a_type="i8", b_type="i8", c_type="i32", compute_type="i32", lda=136,
+                  ldb=272) == ST["NOT_SUPPORTED"]
+    assert chk_sp(a_type="i8", b_type="i8", c_type="i32", compute_type="i32",
+                  lda=132) == ST["NOT_SUPPORTED"]
+    assert chk_sp(a_type="i8", b_type="i8", c_type="f32", compute_type="f32") == ST["NOT_SUPPORTED"]
+    assert chk_sp(a_type="i8", b_type="i8", c_type="i32", compute_type="f32") == ST["NOT_SUPPORTED"]
+    assert chk_sp(a_type="i8", b_type="f16", c_type="i32", compute_type="i32") == ST["NOT_SUPPORTED"]
     assert chk_sp(a_type="e4m3", b_type="e4m3") == ST["NOT_SUPPORTED"]
     assert chk_sp(compute_type="i32") == ST["NOT_SUPPORTED"]
     # k a multiple of 128; k = 0 allowed (D = beta C), with null operands

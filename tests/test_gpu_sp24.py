@@ -201,3 +201,53 @@ def test_sp24_bitexact_free_positions_and_specials(in_type):
 def test_sp24_bitexact_workload():
     w = NEXT_WORKLOADS["f16_sp24_4096_nt"]
     _bitexact(w, points=sample_points(w.m, w.n, 3000))
+
+
+# --------------------------------------------------------------------------------------------
+# INT8 inputs (v_smfmac_i32_16x16x128_i8): exact INT32 results, wrapping like the dense path.
+@pytest.mark.parametrize("tb", [False, True])
+@pytest.mark.parametrize("alpha,beta", [(1, 0), (3, -2)])
+def test_sp24_int8_exact(tb, alpha, beta):
+    """Shapes with odd and even counts of 128-deep INT8 stages (k = 128, 384, 640: a zero stage
+    pads the last pair), ragged m and n, full-range values, C read when beta != 0."""
+    for t, (m, n, k) in enumerate([(300, 200, 384), (256, 256, 256), (1, 1, 128),
+                                   (513, 257, 1024), (255, 129, 640)]):
+        _run(Workload(f"sp_i8_{alpha}_{beta}", "i8", "i32", m, n, k, transb=tb, alpha=alpha,
+                      beta=beta, sparse24=True, a_dist="int_uniform(-128,127)",
+                      b_dist="int_uniform(-128,127)", c_dist="int_uniform(-100000,100000)",
+                      seed=600 + t))
+
+
+@pytest.mark.parametrize("tb", [False, True])
+def test_sp24_int8_free_positions_wrap_and_k0(tb):
+    w = Workload("sp_i8_pos", "i8", "i32", 260, 140, 512, transb=tb, alpha=1 << 20, beta=0,
+                 sparse24=True, a_dist="int_uniform(-128,127)", b_dist="int_uniform(-128,127)",
+                 seed=601)
+    inp = generate(w)
+    rng = np.random.default_rng(601)
+    inp.meta = pack_sp24_meta(rng.integers(0, 4, size=(w.m, w.k // 2)).astype(np.uint8),
+                              w.ld_meta)
+    _run(w, inp=inp)                     # alpha = 2^20: the INT32 epilogue wraps
+    _run(Workload("sp_i8_k0", "i8", "i32", 300, 130, 0, alpha=1, beta=-3, sparse24=True,
+                  c_dist="int_uniform(-1000,1000)", seed=602))
+    _run(Workload("sp_i8_alias", "i8", "i32", 300, 130, 256, alpha=2, beta=1, sparse24=True,
+                  a_dist="int_uniform(-128,127)", b_dist="int_uniform(-128,127)",
+                  c_dist="int_uniform(-1000,1000)", seed=603), in_place=True)
+
+
+@pytest.mark.parametrize("tb", [False, True])
+def test_sp24_int8_padded_strides_and_edges(tb):
+    m, n, k = 256 * 5 + 37, 256 * 3 + 5, 768
+    w = Workload("sp_i8_pad", "i8", "i32", m, n, k, transb=tb, sparse24=True,
+                 lda=k // 2 + 48, ldb=(k if tb else 784) + 32, ldc=776, ld_meta=k // 8 + 32,
+                 a_dist="int_uniform(-128,127)", b_dist="int_uniform(-128,127)", seed=604)
+    ii, jj = sample_points(m, n, 4000, seed=5)
+    rows, cols = [0, m - 2, m - 1], [0, n - 2, n - 1]
+    ii = np.concatenate([ii, np.repeat(rows, n), np.tile(np.arange(m), len(cols))])
+    jj = np.concatenate([jj, np.tile(np.arange(n), len(rows)), np.repeat(cols, m)])
+    _run(w, points=(ii.astype(np.int64), jj.astype(np.int64)))
+
+
+def test_sp24_int8_workload():
+    w = NEXT_WORKLOADS["i8_sp24_4096_nn"]
+    _run(w, points=sample_points(w.m, w.n, 3000))

@@ -167,3 +167,46 @@ def test_points_equal_full():
     pts = oracle.gemm_sp24(False, w.m, w.n, w.k, 1.0, inp.A, "bf16", w.lda, inp.meta,
                            w.ld_meta, inp.B, w.ldb, 0.0, None, "f32", w.ldc, points=(ii, jj))
     assert np.array_equal(pts.v, full.v[ii, jj])
+
+
+@pytest.mark.parametrize("transb", [False, True])
+@pytest.mark.parametrize("alpha,beta", [(1, 0), (3, -2)])
+def test_int8_matches_dense_int_reference_of_decompressed_a(transb, alpha, beta):
+    """INT8: the sparse reference equals the dense INT8 reference of the decompressed A exactly
+    (integers: no ordering question), including INT32 wrap-around with large alpha."""
+    w = Workload("sp_int", "i8", "i32", 33, 27, 256, transb=transb, alpha=alpha, beta=beta,
+                 sparse24=True, a_dist="int_uniform(-128,127)", b_dist="int_uniform(-128,127)",
+                 c_dist="int_uniform(-1000,1000)", seed=13)
+    inp = generate(w)
+    ref = oracle.gemm_sp24_int(transb, w.m, w.n, w.k, alpha, inp.A, w.lda, inp.meta, w.ld_meta,
+                               inp.B, w.ldb, beta, inp.C, w.ldc)
+    idx = _unpack(inp.meta, w.m, w.k)
+    Ad = np.zeros((w.m, w.k), np.int8)
+    j = np.arange(w.k // 2)
+    Ad[np.repeat(np.arange(w.m)[:, None], w.k // 2, 1), 4 * (j // 2) + idx] = inp.A[:, : w.k // 2]
+    dense = oracle.gemm_int(False, transb, w.m, w.n, w.k, alpha, Ad, w.k, inp.B, w.ldb, beta,
+                            inp.C, w.ldc)
+    assert np.array_equal(ref, dense)
+    big = oracle.gemm_sp24_int(transb, w.m, w.n, w.k, 1 << 20, inp.A, w.lda, inp.meta,
+                               w.ld_meta, inp.B, w.ldb, 0, None, w.ldc)
+    plain = oracle.gemm_int(False, transb, w.m, w.n, w.k, 1, Ad, w.k, inp.B, w.ldb, 0, None,
+                            w.ldc).astype(np.int64)        # |sum| < 2^22: no wrap
+    exact = plain * (1 << 20)
+    assert np.array_equal(big, ((exact + (1 << 31)) % (1 << 32) - (1 << 31)).astype(np.int32))
+    assert np.any(np.abs(exact) >= 1 << 31)                 # the wrap is exercised
+
+
+def test_int8_brute_force_any_positions():
+    rng = np.random.default_rng(17)
+    m, n, k = 3, 5, 16
+    idx = rng.integers(0, 4, size=(m, k // 2)).astype(np.uint8)
+    idx[0, :2] = (2, 2)
+    meta = pack_sp24_meta(idx, 16)
+    Ac = rng.integers(-128, 128, size=(m, 16)).astype(np.int8)
+    B = rng.integers(-128, 128, size=(k, 16)).astype(np.int8)
+    C = rng.integers(-50, 50, size=(m, 8)).astype(np.int32)
+    ref = oracle.gemm_sp24_int(False, m, n, k, -2, Ac, 16, meta, 16, B, 16, 5, C, 8)
+    for i in range(m):
+        for c in range(n):
+            s = sum(int(Ac[i, j]) * int(B[4 * (j // 2) + int(idx[i, j]), c]) for j in range(k // 2))
+            assert ref[i, c] == -2 * s + 5 * int(C[i, c])
