@@ -11,6 +11,7 @@ on a bounded sample of the same workload.
   python bench.py --workload e4m3_4096_nt         # FP8 E4M3 inputs
   python bench.py --workload f16_sp24_4096_nt     # 2:4 structured-sparse FP16 A
   python bench.py --workload i8_sp24_4096_nn      # 2:4 structured-sparse INT8 A
+  python bench.py --workload e4m3_sp24_4096_nt    # 2:4 structured-sparse E4M3 A
   python bench.py --copy-calibration   # a plain copy of known size, for counter scaling
 """
 from __future__ import annotations
@@ -284,7 +285,7 @@ def cpu_baseline(w, target_s: float = 15.0):
         elif w.sparse24:
             oracle.gemm_sp24(w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda, inp.meta,
                              w.ld_meta, inp.B, w.ldb, w.beta, inp.C, w.out_type, w.ldc,
-                             points=pts)
+                             points=pts, btype=w.b_type)
         elif w.in_type == "i8":
             oracle.gemm_int(w.transa, w.transb, w.m, w.n, w.k, int(w.alpha), inp.A, w.lda, inp.B,
                             w.ldb, int(w.beta), inp.C, w.ldc, points=pts)

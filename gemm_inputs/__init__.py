@@ -300,6 +300,10 @@ NEXT_WORKLOADS = {
         "i8_sp24_4096_nn", "i8", "i32", 4096, 4096, 4096, alpha=1.0, beta=0.0,
         a_dist="int_uniform(-128,127)", b_dist="int_uniform(-128,127)", seed=12, sparse24=True,
         note="INT8 4096^3 with a 2:4 sparse A (kept values 4096 x 2048), B row-major k x n"),
+    "e4m3_sp24_4096_nt": Workload(
+        "e4m3_sp24_4096_nt", "e4m3", "f32", 4096, 4096, 4096, transb=True, alpha=1.0, beta=0.0,
+        a_dist="normal(0,1)", b_dist="normal(0,1)", seed=14, sparse24=True,
+        note="E4M3 4096^3 with a 2:4 sparse A (kept values 4096 x 2048), B stored n x k"),
     "e4m3_4096_nt": Workload(
         "e4m3_4096_nt", "e4m3", "f32", 4096, 4096, 4096, transb=True, alpha=1.0, beta=0.0,
         a_dist="normal(0,1)", b_dist="normal(0,1)", seed=8,

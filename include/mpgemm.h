@@ -185,7 +185,9 @@ mpgemm_status_t mpgemm_run_bf16x3(mpgemm_handle_t handle, mpgemm_op_t transa,
  *           MPGEMM_R_32F or a_type: numerics as for the dense FP16/BF16 GEMM, over the k/2
  *           kept products (blocks of 8 kept products, in kept order); or a_type = b_type =
  *           MPGEMM_R_8I with compute and c_type MPGEMM_R_32I: exact, wrapping INT32 arithmetic
- *           as for the dense INT8 GEMM (alpha and beta point to int32_t).
+ *           as for the dense INT8 GEMM (alpha and beta point to int32_t); or a_type and b_type
+ *           each MPGEMM_R_8F_E4M3 or MPGEMM_R_8F_E5M2, compute MPGEMM_R_32F, c_type
+ *           MPGEMM_R_32F or MPGEMM_R_16BF: numerics as for the dense FP8 GEMM.
  *   Sizes:  k a multiple of 128 (else MPGEMM_STATUS_NOT_SUPPORTED); m, n arbitrary.
  *   Alignment: Ac, meta, B, C (when read), D 16-byte aligned; rows of Ac and B (lda, ldb
  *           elements) and of the metadata (ld_meta bytes) multiples of 16 bytes, ldc as for

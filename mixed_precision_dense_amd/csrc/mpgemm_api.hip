@@ -343,8 +343,12 @@ mpgemm_status_t mpgemm_check_sp24(mpgemm_op_t transb, int64_t m, int64_t n, int6
     if (!valid_dtype(a_type) || !valid_dtype(b_type) || !valid_dtype(c_type) ||
         !valid_dtype(compute_type))
         return MPGEMM_STATUS_NOT_SUPPORTED;
-    if (a_type != b_type) return MPGEMM_STATUS_NOT_SUPPORTED;
-    if (a_type == MPGEMM_R_8I) {
+    if (is_fp8_type(a_type) && is_fp8_type(b_type)) {
+        if (kernel_out_kind(a_type, b_type, c_type, compute_type) < 0)
+            return MPGEMM_STATUS_NOT_SUPPORTED;
+    } else if (a_type != b_type) {
+        return MPGEMM_STATUS_NOT_SUPPORTED;
+    } else if (a_type == MPGEMM_R_8I) {
         if (compute_type != MPGEMM_R_32I || c_type != MPGEMM_R_32I) return MPGEMM_STATUS_NOT_SUPPORTED;
     } else if (a_type == MPGEMM_R_16F || a_type == MPGEMM_R_16BF) {
         if (compute_type != MPGEMM_R_32F || (c_type != MPGEMM_R_32F && c_type != a_type))
@@ -417,11 +421,12 @@ mpgemm_status_t mpgemm_run_sp24(mpgemm_handle_t handle, mpgemm_op_t transb, int6
     p.tiles_n = (int)((n + mpg::kSpTileN - 1) / mpg::kSpTileN);
     sp.meta = meta;
     sp.ld_meta = ld_meta;
-    const int in = a_type == MPGEMM_R_8I ? mpg::IN_I8
-                                         : (a_type == MPGEMM_R_16F ? mpg::IN_F16 : mpg::IN_BF16);
+    const int in = is_fp8_type(a_type) ? fp8_kind(a_type, b_type)
+                   : a_type == MPGEMM_R_8I ? mpg::IN_I8
+                   : (a_type == MPGEMM_R_16F ? mpg::IN_F16 : mpg::IN_BF16);
     const int out = c_type == MPGEMM_R_32I ? mpg::OUT_I32
                     : c_type == MPGEMM_R_32F ? mpg::OUT_F32
-                    : (a_type == MPGEMM_R_16F ? mpg::OUT_F16 : mpg::OUT_BF16);
+                    : (c_type == MPGEMM_R_16F ? mpg::OUT_F16 : mpg::OUT_BF16);
     const hipError_t e = mpg::launch_sp24(in, out, transb == MPGEMM_OP_T, sp, (hipStream_t)stream);
     return e == hipSuccess ? MPGEMM_STATUS_SUCCESS : MPGEMM_STATUS_LAUNCH_FAILED;
 }

@@ -112,6 +112,10 @@ def _load() -> ctypes.CDLL:
         lib.oracle_gemm_sp24_int_points.restype = i32
         lib.oracle_gemm_sp24_int_points.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64, i64,
                                                     vp, i64, i64, vp, vp, vp]
+        lib.oracle_gemm_sp24_fp8_points.restype = i32
+        lib.oracle_gemm_sp24_fp8_points.argtypes = [i32, i64, dbl, vp, i32, i64, vp, i64, vp, i32,
+                                                    i64, dbl, vp, i32, i64, i64, vp, vp, vp, vp,
+                                                    vp]
         lib.oracle_num_threads.restype = i32
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -395,11 +399,13 @@ def bf16x3_bound(S: np.ndarray, k: int, alpha: float, bc: np.ndarray) -> np.ndar
 def gemm_sp24(transb: bool, m: int, n: int, k: int, alpha: float, Ac: np.ndarray, atype: str,
               lda: int, meta: np.ndarray, ld_meta: int, B: np.ndarray, ldb: int, beta: float,
               C: Optional[np.ndarray], ctype: str, ldc: int,
-              points: Optional[tuple] = None) -> FpReference:
-    """2:4 structured-sparse A (kept values Ac, metadata meta), dense B of the same type:
-    exact products, double sums, as gemm_fp (mpgemm_oracle.c, oracle_gemm_sp24_points)."""
+              points: Optional[tuple] = None, btype: Optional[str] = None) -> FpReference:
+    """2:4 structured-sparse A (kept values Ac, metadata meta), dense B of the same type (FP8:
+    ``btype`` may be the other format): exact products, double sums, as gemm_fp
+    (mpgemm_oracle.c, oracle_gemm_sp24_points / oracle_gemm_sp24_fp8_points)."""
+    btype = atype if btype is None else btype
     _check_storage("A", Ac, atype)
-    _check_storage("B", B, atype)
+    _check_storage("B", B, btype)
     if beta != 0.0:
         _check_storage("C", C, ctype)
     else:
@@ -415,11 +421,18 @@ def gemm_sp24(transb: bool, m: int, n: int, k: int, alpha: float, Ac: np.ndarray
     v = np.empty(ii.shape, np.float64)
     S = np.empty(ii.shape, np.float64)
     bc = np.empty(ii.shape, np.float64)
-    rc = _load().oracle_gemm_sp24_points(int(bool(transb)), k, float(alpha), _ptr(Ac),
-                                         _CODES[atype], lda, meta.ctypes.data, ld_meta, _ptr(B),
-                                         ldb, float(beta), _ptr(C), _CODES[ctype], ldc, ii.size,
-                                         ii.ctypes.data, jj.ctypes.data, v.ctypes.data,
-                                         S.ctypes.data, bc.ctypes.data)
+    if atype in FP8:
+        rc = _load().oracle_gemm_sp24_fp8_points(
+            int(bool(transb)), k, float(alpha), _ptr(Ac), _CODES[atype], lda, meta.ctypes.data,
+            ld_meta, _ptr(B), _CODES[btype], ldb, float(beta), _ptr(C), _CODES[ctype], ldc,
+            ii.size, ii.ctypes.data, jj.ctypes.data, v.ctypes.data, S.ctypes.data,
+            bc.ctypes.data)
+    else:
+        rc = _load().oracle_gemm_sp24_points(int(bool(transb)), k, float(alpha), _ptr(Ac),
+                                             _CODES[atype], lda, meta.ctypes.data, ld_meta,
+                                             _ptr(B), ldb, float(beta), _ptr(C), _CODES[ctype],
+                                             ldc, ii.size, ii.ctypes.data, jj.ctypes.data,
+                                             v.ctypes.data, S.ctypes.data, bc.ctypes.data)
     if rc != 0:
         raise ValueError(f"sparse oracle rejected type {atype}")
     if points is None:

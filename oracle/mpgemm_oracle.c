@@ -901,3 +901,43 @@ int oracle_gemm_sp24_int_points(int transb, int64_t k, int64_t alpha, const int8
     }
     return 0;
 }
+
+/* FP8 (E4M3 / E5M2, either pairing) 2:4 sparse A: as oracle_gemm_sp24_points, the kept
+ * products exact in double, with separate decode tables for A's and B's formats. */
+int oracle_gemm_sp24_fp8_points(int transb, int64_t k, double alpha, const void *Ac, int atype,
+                                int64_t lda, const void *meta, int64_t ld_meta, const void *B,
+                                int btype, int64_t ldb, double beta, const void *C, int ctype,
+                                int64_t ldc, int64_t npts, const int64_t *ii, const int64_t *jj,
+                                double *v, double *S, double *bc)
+{
+    if (!fp8_types_ok(atype, btype, ctype))
+        return -1;
+    double tab_a[256], tab_b[256];
+    for (uint32_t b = 0; b < 256; ++b) {
+        tab_a[b] = decode8(b, atype);
+        tab_b[b] = decode8(b, btype);
+    }
+    const uint8_t *a8 = (const uint8_t *)Ac, *b8 = (const uint8_t *)B, *m8 = (const uint8_t *)meta;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < npts; ++t) {
+        const int64_t i = ii[t], c = jj[t];
+        double s = 0.0, sa = 0.0;
+        for (int64_t j = 0; j < k / 2; ++j) {
+            const int idx = (m8[i * ld_meta + j / 4] >> (2 * (j % 4))) & 3;
+            const double prod = tab_a[a8[i * lda + j]] * tab_b[b8[b_index(transb, ldb, 4 * (j / 2) + idx, c)]];
+            s += prod;
+            sa += fabs(prod);
+        }
+        double betac = 0.0, out;
+        if (beta == 0.0) {
+            out = alpha * s;
+        } else {
+            betac = beta * c_elem(C, ctype, i * ldc + c);
+            out = alpha * s + betac;
+        }
+        v[t] = out;
+        S[t] = sa;
+        bc[t] = betac;
+    }
+    return 0;
+}

@@ -185,7 +185,7 @@ def run_sp24(inp: Inputs, in_place: bool = False, check: bool = True):
     ob = ELEM_BYTES[w.out_type]
     dA = mp.device_buffer(inp.A, w.in_type)
     dM = mp.device_buffer(inp.meta, "i8")
-    dB = mp.device_buffer(inp.B, w.in_type)
+    dB = mp.device_buffer(inp.B, w.b_type)
     d_bytes = (w.m + GUARD_ROWS) * w.ldc * ob
     if in_place:
         cbuf = np.concatenate([inp.C.view(np.uint8).reshape(-1),
@@ -196,7 +196,7 @@ def run_sp24(inp: Inputs, in_place: bool = False, check: bool = True):
         dD = torch.full((d_bytes,), SENTINEL, dtype=torch.uint8, device="cuda")
     compute = "i32" if w.in_type == "i8" else "f32"
     st = mp.mpgemm_run_sp24(handle().h, w.transb, w.m, w.n, w.k, w.alpha, dA, w.in_type, w.lda,
-                            dM, w.ld_meta, dB, w.in_type, w.ldb, w.beta, dC, w.out_type, w.ldc,
+                            dM, w.ld_meta, dB, w.b_type, w.ldb, w.beta, dC, w.out_type, w.ldc,
                             dD, compute, check=check)
     torch.cuda.synchronize()
     raw = dD.cpu().numpy()
@@ -220,7 +220,7 @@ def sp24_ref(inp: Inputs, points=None):
                                     points=points)
     return oracle.gemm_sp24(w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda, inp.meta,
                             w.ld_meta, inp.B, w.ldb, w.beta, inp.C, w.out_type, w.ldc,
-                            points=points)
+                            points=points, btype=w.b_type)
 
 
 def compare_sp24(inp: Inputs, res: GpuResult, exact: bool = False, points=None):
@@ -232,7 +232,7 @@ def compare_sp24(inp: Inputs, res: GpuResult, exact: bool = False, points=None):
     if w.in_type == "i8":
         return oracle.check_int(np.ascontiguousarray(D), sp24_ref(inp, points))
     return oracle.check_fp(np.ascontiguousarray(D), w.out_type, sp24_ref(inp, points),
-                           max(w.k // 2, 1), w.alpha, exact=exact)
+                           max(w.k // 2, 1), w.alpha, exact=exact, fp8=w.in_type in oracle.FP8)
 
 
 def compare_sp24_model(inp: Inputs, res: GpuResult, points=None):

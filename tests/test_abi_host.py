@@ -207,7 +207,13 @@ def test_sp24_contract():
     assert chk_sp(a_type="i8", b_type="i8", c_type="f32", compute_type="f32") == ST["NOT_SUPPORTED"]
     assert chk_sp(a_type="i8", b_type="i8", c_type="i32", compute_type="f32") == ST["NOT_SUPPORTED"]
     assert chk_sp(a_type="i8", b_type="f16", c_type="i32", compute_type="i32") == ST["NOT_SUPPORTED"]
-    assert chk_sp(a_type="e4m3", b_type="e4m3") == ST["NOT_SUPPORTED"]
+    for a in ("e4m3", "e5m2"):
+        for b in ("e4m3", "e5m2"):
+            assert chk_sp(a_type=a, b_type=b, lda=144, ldb=272) == ST["SUCCESS"]
+            assert chk_sp(a_type=a, b_type=b, c_type="bf16", lda=144, ldb=272) == ST["SUCCESS"]
+            assert chk_sp(a_type=a, b_type=b, c_type="f16", lda=144, ldb=272) == ST["NOT_SUPPORTED"]
+            assert chk_sp(a_type=a, b_type=b, lda=136, ldb=272) == ST["NOT_SUPPORTED"]
+    assert chk_sp(a_type="e4m3", b_type="f16") == ST["NOT_SUPPORTED"]
     assert chk_sp(compute_type="i32") == ST["NOT_SUPPORTED"]
     # k a multiple of 128; k = 0 allowed (D = beta C), with null operands
     assert chk_sp(k=200, lda=104, ld_meta=32, ldb=200) == ST["NOT_SUPPORTED"]

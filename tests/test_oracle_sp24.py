@@ -210,3 +210,22 @@ def test_int8_brute_force_any_positions():
         for c in range(n):
             s = sum(int(Ac[i, j]) * int(B[4 * (j // 2) + int(idx[i, j]), c]) for j in range(k // 2))
             assert ref[i, c] == -2 * s + 5 * int(C[i, c])
+
+
+@pytest.mark.parametrize("atype,btype", [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"),
+                                         ("e5m2", "e5m2")])
+@pytest.mark.parametrize("transb", [False, True])
+def test_fp8_matches_dense_fp8_reference_of_decompressed_a(atype, btype, transb):
+    w = Workload("sp_fp8", atype, "f32", 29, 23, 256, transb=transb, alpha=0.5, beta=-1.5,
+                 sparse24=True, a_dist="normal(0,1)", b_dist="normal(0,1)",
+                 c_dist="normal(0,1)", seed=15, b_type=btype)
+    inp = generate(w)
+    ref = oracle.gemm_sp24(transb, w.m, w.n, w.k, w.alpha, inp.A, atype, w.lda, inp.meta,
+                           w.ld_meta, inp.B, w.ldb, w.beta, inp.C, "f32", w.ldc, btype=btype)
+    idx = _unpack(inp.meta, w.m, w.k)
+    Ad = np.zeros((w.m, w.k), np.uint8)
+    j = np.arange(w.k // 2)
+    Ad[np.repeat(np.arange(w.m)[:, None], w.k // 2, 1), 4 * (j // 2) + idx] = inp.A[:, : w.k // 2]
+    dense = oracle.gemm_fp8(False, transb, w.m, w.n, w.k, w.alpha, Ad, atype, w.k, inp.B, btype,
+                            w.ldb, w.beta, inp.C, "f32", w.ldc)
+    assert np.array_equal(ref.v, dense.v) and np.array_equal(ref.S, dense.S)
