@@ -109,7 +109,7 @@ hipError_t launch_split_bf16x3(const float *in, int64_t rows, int64_t cols, int6
     const int64_t threads = iter_rows * row_groups;
     if (threads == 0) return hipSuccess;
     const int64_t blocks = (threads + 255) / 256;
-    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    if (blocks * 256 > (int64_t)UINT32_MAX) return hipErrorInvalidValue;   // 32-bit dispatch size
     hipLaunchKernelGGL(split_bf16x3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in,
                        rows, cols, ld_in, (__bf16 *)out, ld_out, k_along_cols ? 1 : 0, pieces,
                        row_groups, iter_rows);

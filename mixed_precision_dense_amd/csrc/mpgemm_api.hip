@@ -230,8 +230,9 @@ mpgemm_status_t mpgemm_check(mpgemm_op_t transa, mpgemm_op_t transb, int64_t m, 
     if (read_c && !C) return MPGEMM_STATUS_INVALID_VALUE;
     // sizes the kernel indexes with 32-bit integers
     if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return MPGEMM_STATUS_NOT_SUPPORTED;
+    // one workgroup of kThreads per tile (smallest tile), within a 32-bit dispatch size
     const int64_t tiles = ((m + 63) / 64) * ((n + 63) / 64);
-    if (tiles > INT32_MAX) return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (tiles > (int64_t)UINT32_MAX / mpg::kThreads) return MPGEMM_STATUS_NOT_SUPPORTED;
     // alignment contract
     const int ea = elem_bytes(a_type), ec = elem_bytes(c_type);
     if (!aligned16(D) || (read_c && !aligned16(C))) return MPGEMM_STATUS_NOT_SUPPORTED;
@@ -367,6 +368,9 @@ mpgemm_status_t mpgemm_check_sp24(mpgemm_op_t transb, int64_t m, int64_t n, int6
     const bool read_c = !beta_is_zero(beta, compute_type);
     if (!D || (k > 0 && (!Ac || !meta || !B)) || (read_c && !C)) return MPGEMM_STATUS_INVALID_VALUE;
     if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return MPGEMM_STATUS_NOT_SUPPORTED;
+    const int64_t tiles = ((m + mpg::kSpTileM - 1) / mpg::kSpTileM) *
+                          ((n + mpg::kSpTileN - 1) / mpg::kSpTileN);
+    if (tiles > (int64_t)UINT32_MAX / mpg::kThreads) return MPGEMM_STATUS_NOT_SUPPORTED;
     const int ec = elem_bytes(c_type);
     if (!aligned16(D) || (read_c && !aligned16(C))) return MPGEMM_STATUS_NOT_SUPPORTED;
     if (k > 0 && (!aligned16(Ac) || !aligned16(meta) || !aligned16(B))) return MPGEMM_STATUS_NOT_SUPPORTED;
