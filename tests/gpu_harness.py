@@ -257,3 +257,15 @@ def compare_fp8_model(inp: Inputs, res: GpuResult, points=None):
                                w.lda, inp.B, w.b_type, w.ldb, w.beta, inp.C, w.out_type, w.ldc,
                                w.out_type, points=points)
     return oracle.check_bits(np.ascontiguousarray(D), w.out_type, ref)
+
+
+def compare_sp24_fp8_model(inp: Inputs, res: GpuResult, points=None):
+    """Bitwise comparison of a sparse FP8 output with the FP8 block model over kept products."""
+    w = inp.w
+    D = res.D[:, : w.n]
+    if points is not None:
+        D = D[points[0], points[1]]
+    ref = oracle.gemm_sp24_fp8_mfma(w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.in_type, w.lda,
+                                    inp.meta, w.ld_meta, inp.B, w.b_type, w.ldb, w.beta, inp.C,
+                                    w.out_type, w.ldc, w.out_type, points=points)
+    return oracle.check_bits(np.ascontiguousarray(D), w.out_type, ref)
