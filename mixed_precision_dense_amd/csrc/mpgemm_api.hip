@@ -40,6 +40,11 @@ int elem_bytes(mpgemm_dtype_t t) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Largest leading dimension (elements of `eb` bytes) whose 256 rows span at most the
+// 2^31 - 4096 bytes that the kernels' 32-bit buffer offsets reach.  Strides are compared with
+// this bound rather than multiplied out, so that no stride a caller passes can overflow.
+int64_t max_ld(int eb) { return (((int64_t)1 << 31) - 4096) / (256 * (int64_t)eb); }
+
 // Kernel output kind for a supported type combination, or -1.
 int out_kind(mpgemm_dtype_t a, mpgemm_dtype_t b, mpgemm_dtype_t c, mpgemm_dtype_t compute) {
     if (a != b) return -1;
@@ -237,11 +242,9 @@ mpgemm_status_t mpgemm_check(mpgemm_op_t transa, mpgemm_op_t transb, int64_t m, 
     const int ea = elem_bytes(a_type), ec = elem_bytes(c_type);
     if (!aligned16(D) || (read_c && !aligned16(C))) return MPGEMM_STATUS_NOT_SUPPORTED;
     if (k > 0 && (!aligned16(A) || !aligned16(B))) return MPGEMM_STATUS_NOT_SUPPORTED;
-    if ((lda * ea) % 16 || (ldb * ea) % 16 || (ldc * ec) % 16) return MPGEMM_STATUS_NOT_SUPPORTED;
     // every buffer offset the kernel forms spans at most 256 rows of one operand
-    const int64_t limit = (int64_t)1 << 31;
-    if (256 * lda * ea > limit - 4096 || 256 * ldb * ea > limit - 4096 || 256 * ldc * ec > limit - 4096)
-        return MPGEMM_STATUS_NOT_SUPPORTED;
+    if (lda > max_ld(ea) || ldb > max_ld(ea) || ldc > max_ld(ec)) return MPGEMM_STATUS_NOT_SUPPORTED;
+    if ((lda * ea) % 16 || (ldb * ea) % 16 || (ldc * ec) % 16) return MPGEMM_STATUS_NOT_SUPPORTED;
     return MPGEMM_STATUS_SUCCESS;
 }
 
@@ -374,11 +377,9 @@ mpgemm_status_t mpgemm_check_sp24(mpgemm_op_t transb, int64_t m, int64_t n, int6
     const int ec = elem_bytes(c_type);
     if (!aligned16(D) || (read_c && !aligned16(C))) return MPGEMM_STATUS_NOT_SUPPORTED;
     if (k > 0 && (!aligned16(Ac) || !aligned16(meta) || !aligned16(B))) return MPGEMM_STATUS_NOT_SUPPORTED;
-    if ((lda * ea) % 16 || (ldb * ea) % 16 || ld_meta % 16 || (ldc * ec) % 16)
+    if (lda > max_ld(ea) || ldb > max_ld(ea) || ld_meta > max_ld(1) || ldc > max_ld(ec))
         return MPGEMM_STATUS_NOT_SUPPORTED;
-    const int64_t limit = ((int64_t)1 << 31) - 4096;
-    if (256 * lda * ea > limit || 256 * ldb * ea > limit || 256 * ld_meta > limit ||
-        256 * ldc * ec > limit)
+    if ((lda * ea) % 16 || (ldb * ea) % 16 || ld_meta % 16 || (ldc * ec) % 16)
         return MPGEMM_STATUS_NOT_SUPPORTED;
     return MPGEMM_STATUS_SUCCESS;
 }

@@ -138,6 +138,12 @@ def test_alignment_contract():
                lda=72, ldb=64) == ST["NOT_SUPPORTED"]                       # 72 B rows of int8
     # strides whose 256 rows span 2 GiB or more
     assert chk(lda=1 << 22, ldb=64) == ST["NOT_SUPPORTED"]
+    assert chk(lda=(1 << 22) - 8, ldb=64) == ST["SUCCESS"]                  # largest FP16 stride
+    # strides so large that 256 * ld * element size wraps around in 64 bits
+    for big in (1 << 56, 1 << 61, (1 << 63) - 8):
+        assert chk(lda=big) == ST["NOT_SUPPORTED"]
+        assert chk(ldb=big) == ST["NOT_SUPPORTED"]
+        assert chk(ldc=big) == ST["NOT_SUPPORTED"]
 
 
 def test_tile_shape():
@@ -236,6 +242,11 @@ def test_sp24_contract():
     assert chk_sp(m=0, Ac=None, meta=None, B=None, D=None) == ST["SUCCESS"]
     # strides past what 32-bit tile offsets reach
     assert chk_sp(lda=1 << 22) == ST["NOT_SUPPORTED"]
+    for big in (1 << 56, 1 << 61, (1 << 63) - 16):
+        assert chk_sp(lda=big) == ST["NOT_SUPPORTED"]
+        assert chk_sp(ld_meta=big) == ST["NOT_SUPPORTED"]
+        assert chk_sp(ldb=big) == ST["NOT_SUPPORTED"]
+        assert chk_sp(ldc=big) == ST["NOT_SUPPORTED"]
 
 
 def test_sp24_rejects_unknown_handles():
