@@ -110,10 +110,17 @@ hipError_t launch_split_bf16x3(const float *in, int64_t rows, int64_t cols, int6
     if (threads == 0) return hipSuccess;
     const int64_t blocks = (threads + 255) / 256;
     if (blocks * 256 > (int64_t)UINT32_MAX) return hipErrorInvalidValue;   // 32-bit dispatch size
-    hipLaunchKernelGGL(split_bf16x3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in,
-                       rows, cols, ld_in, (__bf16 *)out, ld_out, k_along_cols ? 1 : 0, pieces,
-                       row_groups, iter_rows);
-    return hipGetLastError();
+    // arguments with the kernel's exact parameter types, for hipLaunchKernel (which returns
+    // this launch's own status)
+    const float *a_in = in;
+    __bf16 *a_out = (__bf16 *)out;
+    int a_kc = k_along_cols ? 1 : 0, a_pieces = pieces;
+    int64_t a_rows = rows, a_cols = cols, a_ld_in = ld_in, a_ld_out = ld_out;
+    int64_t a_groups = row_groups, a_iter = iter_rows;
+    void *args[] = {&a_in, &a_rows, &a_cols, &a_ld_in, &a_out, &a_ld_out, &a_kc, &a_pieces,
+                    &a_groups, &a_iter};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&split_bf16x3_kernel),
+                           dim3((unsigned)blocks), dim3(256), args, 0, stream);
 }
 
 }  // namespace mpg

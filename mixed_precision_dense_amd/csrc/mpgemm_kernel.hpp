@@ -844,12 +844,14 @@ void gemm_kernel(Params p) {
     store_tile<IN == IN_I8, OUT, FM, FN, BM, BN>(p, acc, m0, n0, wm, wn, lane, full_mn, m_left, n_left);
 }
 
-// Host-side launcher of one instance.
+// Host-side launcher of one instance.  hipLaunchKernel returns this launch's own status (an
+// error the caller left pending on the thread is neither reported nor cleared).
 template <int IN, int OUT, bool TA, bool TB, int BM, int BN>
 hipError_t launch(const Params &p, hipStream_t stream) {
     const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
-    hipLaunchKernelGGL((gemm_kernel<IN, OUT, TA, TB, BM, BN>), dim3(grid), dim3(kThreads), 0, stream, p);
-    return hipGetLastError();
+    void *args[] = {const_cast<Params *>(&p)};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<IN, OUT, TA, TB, BM, BN>),
+                           dim3(grid), dim3(kThreads), args, 0, stream);
 }
 
 // Entry points of the per-input-type translation units.

@@ -1,13 +1,17 @@
 """GPU parity: the HIP path through the C-ABI against the CPU oracle on the same seeded
 inputs.  INT8 and exactly representable FP cases must match bit for bit; other FP results
 must sit inside the FP32 accumulation bound of the oracle's comparator."""
+import ctypes
+import os
+
 import numpy as np
 import pytest
 import torch
 
 from gemm_inputs import WORKLOADS, Workload, generate, place, sample_points
+import mixed_precision_dense_amd as mp
 import oracle
-from tests.gpu_harness import check_case, compare, run_gpu, say
+from tests.gpu_harness import check_case, compare, handle, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -258,3 +262,28 @@ def test_determinism_bitwise():
     for _ in range(3):
         again = run_gpu(inp, repeat=3).D
         assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+
+
+def test_error_left_pending_by_the_caller_does_not_fail_the_launch():
+    """A HIP error the caller left pending on the thread (here from hipSetDevice on a device
+    that does not exist) is neither returned as the launch's status nor stops the GEMM."""
+    hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD)   # the runtime already loaded
+    w = Workload("pending", "f16", "f32", 100, 72, 64, a_dist="normal(0,1)",
+                 b_dist="normal(0,1)", seed=56)
+    inp = generate(w)
+    want = run_gpu(inp).D
+    dA = mp.device_buffer(inp.A, "f16")
+    dB = mp.device_buffer(inp.B, "f16")
+    dD = torch.zeros(w.m * w.ldc, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+    try:
+        st = mp.mpgemm_run(handle().h, w.transa, w.transb, w.m, w.n, w.k, w.alpha, dA, "f16",
+                           w.lda, dB, "f16", w.ldb, w.beta, None, "f32", w.ldc, dD, "f32",
+                           check=False)
+    finally:
+        hip.hipGetLastError()   # leave nothing pending for torch's own launch checks
+    assert st == mp.SUCCESS
+    torch.cuda.synchronize()
+    got = dD.cpu().numpy().reshape(w.m, w.ldc)
+    assert np.array_equal(got[:, :w.n].view(np.uint32), want[:, :w.n].view(np.uint32))
