@@ -287,3 +287,18 @@ def test_error_left_pending_by_the_caller_does_not_fail_the_launch():
     torch.cuda.synchronize()
     got = dD.cpu().numpy().reshape(w.m, w.ldc)
     assert np.array_equal(got[:, :w.n].view(np.uint32), want[:, :w.n].view(np.uint32))
+
+
+@pytest.mark.parametrize("in_type,out_type", [("f16", "f32"), ("i8", "i32")])
+def test_largest_accepted_strides_mn_contiguous(in_type, out_type):
+    """A stored k x m and B stored k x n at the largest leading dimension the argument check
+    accepts (256 rows just under 2 GiB), on 256 x 256 tiles: every offset of the 32-bit buffer
+    addressing within a stage stays in range (exact small integers, sampled outputs)."""
+    eb = 2 if in_type == "f16" else 1
+    ld = ((1 << 31) - 4096) // (256 * eb)
+    assert (ld * eb) % 16 == 0
+    w = Workload(f"maxld_{in_type}", in_type, out_type, 4096, 3072, 128, transa=True,
+                 lda=ld, ldb=ld, a_dist="int_uniform(-3,3)", b_dist="int_uniform(-3,3)",
+                 seed=57)
+    rep, res = check_case(w, exact=True, sample=20000)
+    _assert(rep, res)

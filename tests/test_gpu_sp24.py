@@ -321,3 +321,18 @@ def test_sp24_fp8_bitexact_workload():
     pts = sample_points(w.m, w.n, 3000)
     rep = compare_sp24_fp8_model(inp, res, points=pts)
     assert rep.ok, f"{rep.n_bad}/{rep.n} differ from the model; {rep.detail}"
+
+
+@pytest.mark.parametrize("which", ["lda", "ld_meta", "ldc"])
+def test_sp24_largest_accepted_strides(which):
+    """Kept values, metadata or D at the largest leading dimension the argument check accepts
+    (256 rows just under 2 GiB): the second tile row starts that far on and every in-tile
+    offset of the 32-bit buffer addressing stays in range.  Bit-exact against the sparse
+    block model."""
+    limit = (1 << 31) - 4096
+    big = {"lda": limit // (256 * 2), "ld_meta": limit // 256, "ldc": limit // (256 * 4)}
+    w = Workload(f"sp_maxld_{which}", "f16", "f32", 300, 72, 256, transb=True, sparse24=True,
+                 a_dist="normal(0,1)", b_dist="normal(0,1)", seed=58, **{which: big[which]})
+    inp, res = _run(w)
+    rep = compare_sp24_model(inp, res)
+    assert rep.ok, f"{rep.n_bad}/{rep.n} differ from the model; {rep.detail}"
