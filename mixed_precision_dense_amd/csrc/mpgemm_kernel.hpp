@@ -118,6 +118,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
                                              0x00020000);
 }
 
+// An empty statement that uses a value held in scalar registers.  Placed where the value is
+// computed (between two MFMAs), it keeps the compiler from sinking that scalar work past the
+// k-tail branch into the block just before the next barrier, where the matrix cores would sit
+// idle while it issues.
+template <typename T>
+__device__ __forceinline__ void keep_here(const T &v) {
+    asm volatile("" : : "s"(v));
+}
+
 // The same raw-buffer descriptor as four dwords, for the direct-to-LDS load below.
 __device__ __forceinline__ i32x4 make_rsrc_words(const void *base) {
     const uint64_t a = (uint64_t)base;
@@ -327,7 +336,10 @@ struct StageCursor {
     // Resource for stage s of nk: every byte before the last stage, exact for the last
     // stage, none past it.
     __device__ __forceinline__ i32x4 rsrc(int s, int nk) const {
-        const int nr = s < nk - 1 ? kNumRecords : (s == nk - 1 ? last_records : 0);
+        return words(s < nk - 1 ? kNumRecords : (s == nk - 1 ? last_records : 0));
+    }
+    // The resource of the next stage with record count nr.
+    __device__ __forceinline__ i32x4 words(int nr) const {
         i32x4 r;
         r[0] = (int)(uint32_t)base;
         r[1] = (int)((uint32_t)(base >> 32) & 0xFFFFu);   // stride 0, no swizzle
@@ -642,9 +654,23 @@ void gemm_kernel(Params p) {
                 opb.load(rs_b, lds_w + (uint32_t)(kBuffers * A_BYTES + parity * B_BYTES), l - OpA::kSlots);
         };
         // Prepare the resources of stage s (the cursors then move to stage s + 1).
-        auto next_rsrc_a = [&](int s) { rs_a = ca.rsrc(s, nk); ca.advance(); };
-        auto next_rsrc_b = [&](int s) { rs_b = cb.rsrc(s, nk); cb.advance(); };
+        auto next_rsrc_a = [&](int s) { rs_a = ca.rsrc(s, nk); ca.advance(); keep_here(rs_a); keep_here(ca.base); };
+        auto next_rsrc_b = [&](int s) { rs_b = cb.rsrc(s, nk); cb.advance(); keep_here(rs_b); keep_here(cb.base); };
         auto no_hook = [&](auto) {};
+        // In the loop the same resources are prepared in eight pieces of one or two scalar
+        // instructions (for A, then B: the record count in two selects, the words, the
+        // advance), each pinned in its own gap between MFMAs.
+        int nr_a = 0, nr_b = 0;
+        auto rsrc_piece = [&](auto p_c, int s) {
+            constexpr int p = decltype(p_c)::value;
+            StageCursor &c = p < 4 ? ca : cb;
+            int &nr = p < 4 ? nr_a : nr_b;
+            i32x4 &rs = p < 4 ? rs_a : rs_b;
+            if constexpr (p % 4 == 0) { nr = s == nk - 1 ? c.last_records : 0; keep_here(nr); }
+            if constexpr (p % 4 == 1) { nr = s < nk - 1 ? kNumRecords : nr; keep_here(nr); }
+            if constexpr (p % 4 == 2) { rs = c.words(nr); keep_here(rs); }
+            if constexpr (p % 4 == 3) { c.advance(); keep_here(c.base); }
+        };
 
         // One k step: the FM x FN MFMAs of fragment set `set`, each in its own fenced group with at
         // most two other instructions -- a wave issues one instruction per four cycles, so more
@@ -691,8 +717,12 @@ void gemm_kernel(Params p) {
             constexpr int P = decltype(par_c)::value;
             k_step(C0{}, P, 1, 0, C0{}, [&](auto idx_c) {
                 constexpr int idx = decltype(idx_c)::value;
-                if constexpr (idx == 1 % kMf) next_rsrc_a(s + 2);
-                if constexpr (idx == 3 % kMf) next_rsrc_b(s + 2);
+                static_for<8>([&](auto p_c) {
+                    // the odd MFMAs of the second half, which have no fragment reads beside them
+                    constexpr int p = decltype(p_c)::value;
+                    constexpr int at = kMf >= 16 ? (kMf / 2 + 1 + 2 * p) % kMf : 1 % kMf;
+                    if constexpr (at == idx) rsrc_piece(p_c, s + 2);
+                });
             });
             wait_vmem<0>();  // this wave's loads of stage s + 1 have landed
             fix_stage(s + 1, P ^ 1);
@@ -749,8 +779,8 @@ void gemm_kernel(Params p) {
             else
                 opb.load(rs_b, lds_w + (uint32_t)(kBuffers * A_BYTES + parity * B_BYTES), l - OpA::kSlots);
         };
-        auto next_rsrc_a = [&](int s) { rs_a = ca.rsrc(s, nk); ca.advance(); };
-        auto next_rsrc_b = [&](int s) { rs_b = cb.rsrc(s, nk); cb.advance(); };
+        auto next_rsrc_a = [&](int s) { rs_a = ca.rsrc(s, nk); ca.advance(); keep_here(rs_a); keep_here(ca.base); };
+        auto next_rsrc_b = [&](int s) { rs_b = cb.rsrc(s, nk); cb.advance(); keep_here(rs_b); keep_here(cb.base); };
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;
 
