@@ -252,3 +252,23 @@ def test_sp24_contract():
 def test_sp24_rejects_unknown_handles():
     assert mp.mpgemm_run_sp24(0x1000, True, 8, 8, 128, 1.0, P, "f16", 64, P, 16, P, "f16", 128,
                               0.0, None, "f32", 8, P, stream=0, check=False) == ST["NOT_INITIALIZED"]
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without the built HIP library every entry point of the binding raises: there is no
+    fallback path."""
+    monkeypatch.setattr(mp, "_lib", None)
+    monkeypatch.setattr(mp, "LIB_PATH", "/nonexistent/libmpgemm.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        mp.load()
+    with pytest.raises(RuntimeError, match="not built"):
+        mp.Handle()
+    with pytest.raises(RuntimeError, match="not built"):
+        mp.mpgemm_run(0x1000, False, False, 8, 8, 8, 1.0, 16, "f16", 8, 16, "f16", 8, 0.0,
+                      None, "f32", 8, 16, "f32", stream=0)
+    with pytest.raises(RuntimeError, match="not built"):
+        mp.mpgemm_run_sp24(0x1000, True, 8, 8, 128, 1.0, 16, "f16", 64, 16, 16, 16, "f16", 128,
+                           0.0, None, "f32", 8, 16, stream=0)
+    with pytest.raises(RuntimeError, match="not built"):
+        mp.mpgemm_check(False, False, 8, 8, 8, 1.0, 16, "f16", 8, 16, "f16", 8, 0.0, None,
+                        "f32", 8, 16, "f32")
