@@ -74,7 +74,8 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
 
 
 def time_gemm(w, steps: int, warmup: int):
-    """Returns (wall ms per step, kernel ms per launch from HIP events, tile)."""
+    """Returns (wall ms per step, kernel ms per launch from HIP events, tile, median kernel ms
+    per launch with cold caches)."""
     import torch
     import mixed_precision_dense_amd as mp
     from gemm_inputs import generate
