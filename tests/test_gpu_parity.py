@@ -302,3 +302,31 @@ def test_largest_accepted_strides_mn_contiguous(in_type, out_type):
                  seed=57)
     rep, res = check_case(w, exact=True, sample=20000)
     _assert(rep, res)
+
+
+@pytest.mark.parametrize("dist,exact", [("int_uniform(-3,3)", True), ("normal(0,1)", False)])
+def test_column_major_caller_through_the_operand_swap(dist, exact):
+    """A column-major caller (the CUDA 9 page's cuBLAS example: lda = M, ldb = K, ldc = M)
+    obtains D^T = op(B)^T op(A)^T by passing (transb, transa, n, m, k, B, ldb, A, lda).  Read
+    back column-major, D matches the oracle evaluated on the column-major operands directly
+    (through its transposed-storage flags, without the swap)."""
+    from gemm_inputs import draw
+    M, N, K = 304, 200, 136
+    rng = np.random.Generator(np.random.PCG64(59))
+    Acm = draw(rng, (K, M), dist, "f16")           # M x K, column-major: a(i, p) = Acm[p, i]
+    Bcm = draw(rng, (N, K), dist, "f16")           # K x N, column-major: b(p, j) = Bcm[j, p]
+    Ccm = draw(rng, (N, M), dist, "f32")           # M x N, column-major: c(i, j) = Ccm[j, i]
+    alpha, beta = 1.0, 0.5
+    say(f"[gpu case] column-major caller M={M} N={N} K={K} {dist}")
+    dA = mp.device_buffer(Acm, "f16")
+    dB = mp.device_buffer(Bcm, "f16")
+    dC = mp.device_buffer(Ccm, "f32")
+    dD = torch.empty(N * M * 4, dtype=torch.uint8, device="cuda")
+    mp.mpgemm_run(handle().h, False, False, N, M, K, alpha, dB, "f16", K, dA, "f16", M, beta,
+                  dC, "f32", M, dD, "f32")
+    torch.cuda.synchronize()
+    D = dD.cpu().numpy().view(np.float32).reshape(N, M).T      # back to M x N
+    ref = oracle.gemm_fp(True, True, M, N, K, alpha, Acm, "f16", M, Bcm, "f16", K, beta,
+                         np.ascontiguousarray(Ccm.T), "f32", N)
+    rep = oracle.check_fp(np.ascontiguousarray(D), "f32", ref, K, alpha, exact=exact)
+    assert rep.ok, f"{rep.n_bad}/{rep.n} bad; {rep.detail}"
