@@ -1,10 +1,27 @@
 """The shared input generator: rounding of draws, layout, padding sentinels and seeding.
 CPU only."""
+import hashlib
+import os
+
 import numpy as np
+import pytest
 
 import oracle
-from gemm_inputs import (WORKLOADS, Workload, f64_to_bf16_bits, f64_to_f16_bits, generate,
-                         sample_points)
+from gemm_inputs import (NEXT_WORKLOADS, WORKLOADS, Workload, f64_to_bf16_bits,
+                         f64_to_f16_bits, generate, sample_points)
+
+DIGESTS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "input_digests.txt")
+
+
+def _recorded_digests():
+    rows = {}
+    with open(DIGESTS) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, label, dtype, shape, digest = line.split()
+            rows.setdefault(name, []).append((label, dtype, shape, digest))
+    return rows
 
 
 def test_bf16_rounding_agrees_with_oracle_encoder():
@@ -66,3 +83,20 @@ def test_log_uniform_spreads_over_binades():
     assert 0.45 < np.mean(x > 0) < 0.55
     y = draw(np.random.Generator(np.random.PCG64(3)), (200, 300), "log_uniform(-20,10)", "f16")
     assert np.array_equal(y.view(np.uint16), x.astype(np.float16).view(np.uint16))
+
+
+def test_every_workload_has_recorded_digests():
+    assert set(_recorded_digests()) == set(WORKLOADS) | set(NEXT_WORKLOADS)
+
+
+@pytest.mark.parametrize("name", sorted(set(WORKLOADS) | set(NEXT_WORKLOADS)))
+def test_input_buffers_match_their_recorded_digests(name):
+    """Each named workload's seeded buffers hash to the SHA-256 recorded when the workloads
+    were fixed (golden/input_digests.txt, written by golden/make_input_digests.py from the
+    generator alone): the same inputs on every machine and run."""
+    w = WORKLOADS.get(name) or NEXT_WORKLOADS[name]
+    inp = generate(w)
+    for label, dtype, shape, digest in _recorded_digests()[name]:
+        arr = getattr(inp, label)
+        assert str(arr.dtype) == dtype and "x".join(map(str, arr.shape)) == shape, (name, label)
+        assert hashlib.sha256(arr.tobytes()).hexdigest() == digest, (name, label)
