@@ -84,14 +84,19 @@ def _dtype(t: Union[str, int]) -> int:
 
 def _op(t: Union[bool, int, str]) -> int:
     if isinstance(t, str):
+        if t.upper() not in ("N", "T"):
+            raise ValueError(f"transpose flag {t!r}: expected 'N' or 'T'")
         return OP_T if t.upper() == "T" else OP_N
     return OP_T if t else OP_N
 
 
 def _ptr(x) -> Optional[int]:
+    """Device address of a tensor (which must live on a GPU), or an integer address as is."""
     if x is None:
         return None
     if isinstance(x, torch.Tensor):
+        if not x.is_cuda:
+            raise ValueError(f"tensor on {x.device}: the kernels read and write device memory")
         return x.data_ptr()
     return int(x)
 

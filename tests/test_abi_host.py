@@ -272,3 +272,16 @@ def test_missing_library_fails_loudly(monkeypatch):
     with pytest.raises(RuntimeError, match="not built"):
         mp.mpgemm_check(False, False, 8, 8, 8, 1.0, 16, "f16", 8, 16, "f16", 8, 0.0, None,
                         "f32", 8, 16, "f32")
+
+
+def test_binding_rejects_host_tensors_and_unknown_flags():
+    """A CPU tensor would hand a host address to the kernels; an unknown transpose letter would
+    silently mean N.  Both are refused before the library is called."""
+    cpu = torch.zeros(64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="device memory"):
+        mp.mpgemm_check(False, False, 8, 8, 8, 1.0, cpu, "f16", 8, P, "f16", 8, 0.0, None, "f32",
+                        8, P, "f32")
+    with pytest.raises(ValueError, match="'N' or 'T'"):
+        mp.mpgemm_check("X", False, 8, 8, 8, 1.0, P, "f16", 8, P, "f16", 8, 0.0, None, "f32", 8,
+                        P, "f32")
+    assert chk(transa="t", transb="N") == ST["SUCCESS"]
