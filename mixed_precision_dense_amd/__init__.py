@@ -104,6 +104,8 @@ def _ptr(x) -> Optional[int]:
 def _scalar(v, compute_type: int):
     """alpha / beta as the compute type's host scalar (float or int32_t)."""
     if compute_type == R_32I:
+        if not -(1 << 31) <= int(v) < (1 << 31):
+            raise ValueError(f"integer scalar {v} does not fit in int32")
         return ctypes.c_int32(int(v))
     return ctypes.c_float(float(v))
 
