@@ -286,6 +286,6 @@ def test_binding_rejects_host_tensors_and_unknown_flags():
                         P, "f32")
     assert chk(transa="t", transb="N") == ST["SUCCESS"]
     i8 = dict(a_type="i8", b_type="i8", c_type="i32", compute_type="i32", lda=64, ldb=64)
-    assert chk(alpha=(1 << 31) - 1, beta=-(1 << 31), **i8) == ST["SUCCESS"]
+    assert chk(alpha=(1 << 31) - 1, beta=-(1 << 31), C=P, **i8) == ST["SUCCESS"]
     with pytest.raises(ValueError, match="int32"):
         chk(alpha=1 << 31, beta=0, **i8)
