@@ -231,8 +231,10 @@ mpgemm_status_t mpgemm_destroy(mpgemm_handle_t handle);
 const char *mpgemm_status_string(mpgemm_status_t status);
 
 /* Tile shape (rows x columns of D per workgroup) that mpgemm_run picks for an m x n output
- * with inputs of type a_type, written to *tile_m and *tile_n.  Host-only; for diagnostics and
- * benchmarks.  Returns MPGEMM_STATUS_INVALID_VALUE for negative sizes or null outputs. */
+ * with inputs of type a_type on a device with 256 compute units (a whole MI355X; mpgemm_run
+ * uses the handle's device's count), written to *tile_m and *tile_n.  Host-only; for
+ * diagnostics and benchmarks.  Returns MPGEMM_STATUS_INVALID_VALUE for negative sizes or null
+ * outputs. */
 mpgemm_status_t mpgemm_tile_shape(int64_t m, int64_t n, mpgemm_dtype_t a_type, int *tile_m,
                                   int *tile_n);
 

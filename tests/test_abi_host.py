@@ -151,6 +151,11 @@ def test_tile_shape():
     assert mp.mpgemm_tile_shape(256, 256) == (64, 64)
     assert mp.mpgemm_tile_shape(256, 256, "i8") == (128, 128)
     assert mp.mpgemm_tile_shape(5000, 3000) == (256, 256)
+    # one round of 144 large tiles beats three rounds of 576 half-size ones
+    assert mp.mpgemm_tile_shape(3072, 3072) == (256, 256)
+    assert mp.mpgemm_tile_shape(2048, 2048) == (128, 128)   # 64 large tiles would idle 3/4 of the CUs
+    assert mp.mpgemm_tile_shape(1024, 1024) == (64, 64)
+    assert mp.mpgemm_tile_shape(1024, 1024, "e4m3") == (128, 128)
 
 
 def test_bf16x3_workspace_size():
