@@ -330,3 +330,14 @@ def test_column_major_caller_through_the_operand_swap(dist, exact):
                          np.ascontiguousarray(Ccm.T), "f32", N)
     rep = oracle.check_fp(np.ascontiguousarray(D), "f32", ref, K, alpha, exact=exact)
     assert rep.ok, f"{rep.n_bad}/{rep.n} bad; {rep.detail}"
+
+
+@pytest.mark.parametrize("n", [2560, 3072])
+def test_shapes_on_one_partial_round_of_large_tiles(n):
+    """Squares that the tile rule puts on one round of 256 x 256 tiles with part of the chip
+    idle (100 and 144 workgroups): exact integer inputs, sampled outputs against the oracle."""
+    assert mp.mpgemm_tile_shape(n, n, "f16") == (256, 256)
+    w = Workload(f"round_{n}", "f16", "f32", n, n, n, transb=True, a_dist="int_uniform(-2,2)",
+                 b_dist="int_uniform(-2,2)", seed=60)
+    rep, res = check_case(w, exact=True, sample=20000)
+    _assert(rep, res)
