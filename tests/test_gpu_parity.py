@@ -341,3 +341,40 @@ def test_shapes_on_one_partial_round_of_large_tiles(n):
                  b_dist="int_uniform(-2,2)", seed=60)
     rep, res = check_case(w, exact=True, sample=20000)
     _assert(rep, res)
+
+
+def test_captured_in_a_graph_every_replay_matches_eager():
+    """mpgemm_run queued under HIP graph capture (torch.cuda.graph): the call makes no
+    allocation, memset or synchronisation, so the captured launch replays.  Each replay, with
+    eager work and synchronisations between them, reproduces the eager result bit for bit."""
+    w = Workload("graph", "f16", "f32", 256, 256, 256, alpha=1.0, beta=1.0,
+                 a_dist="uniform(-1,1)", b_dist="uniform(-1,1)", c_dist="uniform(-1,1)", seed=61)
+    inp = generate(w)
+    dA = mp.device_buffer(inp.A, "f16")
+    dB = mp.device_buffer(inp.B, "f16")
+    dC = mp.device_buffer(inp.C, "f32")
+    dD = torch.empty(w.m * w.ldc, dtype=torch.float32, device="cuda")
+
+    def call():
+        mp.mpgemm_run(handle().h, False, False, w.m, w.n, w.k, w.alpha, dA, "f16", w.lda, dB,
+                      "f16", w.ldb, w.beta, dC, "f32", w.ldc, dD, "f32")
+
+    call()
+    torch.cuda.synchronize()
+    want = dD.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):      # a first call on a side stream before capture
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(4):
+        dD.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dD.view(torch.int32), want.view(torch.int32))
+    say("[gpu case] graph capture: 4 replays bit-identical to the eager call")
