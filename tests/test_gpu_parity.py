@@ -343,21 +343,50 @@ def test_shapes_on_one_partial_round_of_large_tiles(n):
     _assert(rep, res)
 
 
-def test_captured_in_a_graph_every_replay_matches_eager():
-    """mpgemm_run queued under HIP graph capture (torch.cuda.graph): the call makes no
-    allocation, memset or synchronisation, so the captured launch replays.  Each replay, with
-    eager work and synchronisations between them, reproduces the eager result bit for bit."""
-    w = Workload("graph", "f16", "f32", 256, 256, 256, alpha=1.0, beta=1.0,
-                 a_dist="uniform(-1,1)", b_dist="uniform(-1,1)", c_dist="uniform(-1,1)", seed=61)
-    inp = generate(w)
-    dA = mp.device_buffer(inp.A, "f16")
-    dB = mp.device_buffer(inp.B, "f16")
-    dC = mp.device_buffer(inp.C, "f32")
-    dD = torch.empty(w.m * w.ldc, dtype=torch.float32, device="cuda")
+@pytest.mark.parametrize("entry", ["mpgemm_run", "mpgemm_run_sp24", "mpgemm_run_bf16x3"])
+def test_captured_in_a_graph_every_replay_matches_eager(entry):
+    """Each entry point queued under HIP graph capture (torch.cuda.graph): the calls make no
+    allocation, memset or synchronisation (the three-product GEMM's workspace is the caller's),
+    so the captured launches replay.  Each replay, with eager work and synchronisations between
+    them, reproduces the eager result bit for bit."""
+    h = handle().h
+    if entry == "mpgemm_run_sp24":
+        w = Workload("graph_sp", "f16", "f32", 256, 256, 256, transb=True, sparse24=True,
+                     alpha=1.0, beta=1.0, a_dist="uniform(-1,1)", b_dist="uniform(-1,1)",
+                     c_dist="uniform(-1,1)", seed=62)
+        inp = generate(w)
+        dA, dM = mp.device_buffer(inp.A, "f16"), mp.device_buffer(inp.meta, "i8")
+        dB, dC = mp.device_buffer(inp.B, "f16"), mp.device_buffer(inp.C, "f32")
+        dD = torch.empty(w.m * w.ldc, dtype=torch.float32, device="cuda")
 
-    def call():
-        mp.mpgemm_run(handle().h, False, False, w.m, w.n, w.k, w.alpha, dA, "f16", w.lda, dB,
-                      "f16", w.ldb, w.beta, dC, "f32", w.ldc, dD, "f32")
+        def call():
+            mp.mpgemm_run_sp24(h, w.transb, w.m, w.n, w.k, w.alpha, dA, "f16", w.lda, dM,
+                               w.ld_meta, dB, "f16", w.ldb, w.beta, dC, "f32", w.ldc, dD, "f32")
+    elif entry == "mpgemm_run_bf16x3":
+        w = Workload("graph_3", "f32", "f32", 256, 256, 256, alpha=1.0, beta=1.0,
+                     a_dist="normal(0,1)", b_dist="normal(0,1)", c_dist="normal(0,1)", seed=63)
+        inp = generate(w)
+        dA, dB, dC = (mp.device_buffer(x, "f32") for x in (inp.A, inp.B, inp.C))
+        dD = torch.empty(w.m * w.ldc, dtype=torch.float32, device="cuda")
+        need = mp.mpgemm_bf16x3_workspace_size(False, False, w.m, w.n, w.k)
+        ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+        ws_ptr = (ws.data_ptr() + 255) // 256 * 256
+
+        def call():
+            mp.mpgemm_run_bf16x3(h, False, False, w.m, w.n, w.k, w.alpha, dA, w.lda, dB, w.ldb,
+                                 w.beta, dC, w.ldc, dD, ws_ptr, need)
+    else:
+        w = Workload("graph", "f16", "f32", 256, 256, 256, alpha=1.0, beta=1.0,
+                     a_dist="uniform(-1,1)", b_dist="uniform(-1,1)", c_dist="uniform(-1,1)",
+                     seed=61)
+        inp = generate(w)
+        dA, dB = mp.device_buffer(inp.A, "f16"), mp.device_buffer(inp.B, "f16")
+        dC = mp.device_buffer(inp.C, "f32")
+        dD = torch.empty(w.m * w.ldc, dtype=torch.float32, device="cuda")
+
+        def call():
+            mp.mpgemm_run(h, False, False, w.m, w.n, w.k, w.alpha, dA, "f16", w.lda, dB, "f16",
+                          w.ldb, w.beta, dC, "f32", w.ldc, dD, "f32")
 
     call()
     torch.cuda.synchronize()
@@ -377,4 +406,4 @@ def test_captured_in_a_graph_every_replay_matches_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(dD.view(torch.int32), want.view(torch.int32))
-    say("[gpu case] graph capture: 4 replays bit-identical to the eager call")
+    say(f"[gpu case] graph capture of {entry}: 4 replays bit-identical to the eager call")
