@@ -52,7 +52,9 @@
  *
  * Alignment contract (there is no slower fallback path): A, B, C (when read) and D must be
  * 16-byte aligned, and lda, ldb, ldc times the element size must be multiples of 16 bytes
- * (8 elements for FP16/BF16, 16 for INT8 and FP8, 4 for FP32/INT32).  m, n and k are arbitrary.
+ * (8 elements for FP16/BF16, 16 for INT8 and FP8, 4 for FP32/INT32).  m, n and k are
+ * arbitrary up to 2^31 - 1 (k up to 2^31 - 256); larger sizes return
+ * MPGEMM_STATUS_NOT_SUPPORTED.
  * Operands are read in whole aligned 16-byte blocks: each row of A and B must be readable up
  * to the end of the 16-byte block holding its last element (true of any buffer whose size is
  * rows * ld elements).  Elements beyond the logical row are never used in the result.
@@ -165,6 +167,15 @@ mpgemm_status_t mpgemm_run_bf16x3(mpgemm_handle_t handle, mpgemm_op_t transa,
                                   const float *B, int64_t ldb, const float *beta,
                                   const float *C, int64_t ldc, float *D, void *workspace,
                                   uint64_t workspace_bytes, void *stream);
+
+/* Host-only argument check of mpgemm_run_bf16x3: returns exactly the status mpgemm_run_bf16x3
+ * would return for these arguments before touching the device (the workspace's size and
+ * alignment included); needs no handle and no device, and dereferences only alpha and beta. */
+mpgemm_status_t mpgemm_check_bf16x3(mpgemm_op_t transa, mpgemm_op_t transb, int64_t m,
+                                    int64_t n, int64_t k, const float *alpha, const float *A,
+                                    int64_t lda, const float *B, int64_t ldb, const float *beta,
+                                    const float *C, int64_t ldc, const float *D,
+                                    const void *workspace, uint64_t workspace_bytes);
 
 /* GEMM with a 2:4 structured-sparse A (the page "稀疏张量核心加速模板计算的技术解析" on sparse tensor
  * cores for stencils, sections

@@ -38,6 +38,39 @@ class MpgemmError(RuntimeError):
         super().__init__(f"{what}: {STATUS.get(status, status)} ({status_string(status)})")
 
 
+_i64, _i32, _u64, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p
+# (restype, argtypes) of every function include/mpgemm.h declares
+SIGNATURES = {
+    "mpgemm_create": (_i32, [ctypes.POINTER(_vp)]),
+    "mpgemm_destroy": (_i32, [_vp]),
+    "mpgemm_run": (_i32, [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _i32,
+                          _i64, _vp, _vp, _i32, _i64, _vp, _i32, _vp]),
+    "mpgemm_check": (_i32, [_i32, _i32, _i64, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _i32, _i64,
+                            _vp, _vp, _i32, _i64, _vp, _i32]),
+    "mpgemm_status_string": (ctypes.c_char_p, [_i32]),
+    "mpgemm_tile_shape": (_i32, [_i64, _i64, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "mpgemm_run_sp24": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _vp,
+                               _i32, _i64, _vp, _vp, _i32, _i64, _vp, _i32, _vp]),
+    "mpgemm_check_sp24": (_i32, [_i32, _i64, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _vp,
+                                 _i32, _i64, _vp, _vp, _i32, _i64, _vp, _i32]),
+    "mpgemm_run_bf16x3": (_i32, [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64,
+                                 _vp, _vp, _i64, _vp, _vp, _u64, _vp]),
+    "mpgemm_check_bf16x3": (_i32, [_i32, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
+                                   _vp, _i64, _vp, _vp, _u64]),
+    "mpgemm_bf16x3_workspace_size": (_u64, [_i32, _i32, _i64, _i64, _i64]),
+}
+
+
+def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Set the C signature of every ABI function the loaded library exports."""
+    for name, (res, args) in SIGNATURES.items():
+        if hasattr(lib, name):
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+    return lib
+
+
 def load() -> ctypes.CDLL:
     """Load the built library (raises if it has not been built)."""
     global _lib
@@ -45,35 +78,7 @@ def load() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run mixed_precision_dense_amd/build.py "
                                "(or __graft_entry__.build())")
-        lib = ctypes.CDLL(LIB_PATH)
-        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
-        lib.mpgemm_create.restype = i32
-        lib.mpgemm_create.argtypes = [ctypes.POINTER(vp)]
-        lib.mpgemm_destroy.restype = i32
-        lib.mpgemm_destroy.argtypes = [vp]
-        lib.mpgemm_run.restype = i32
-        lib.mpgemm_run.argtypes = [vp, i32, i32, i64, i64, i64, vp, vp, i32, i64, vp, i32, i64,
-                                   vp, vp, i32, i64, vp, i32, vp]
-        lib.mpgemm_check.restype = i32
-        lib.mpgemm_check.argtypes = [i32, i32, i64, i64, i64, vp, vp, i32, i64, vp, i32, i64,
-                                     vp, vp, i32, i64, vp, i32]
-        lib.mpgemm_status_string.restype = ctypes.c_char_p
-        lib.mpgemm_status_string.argtypes = [i32]
-        lib.mpgemm_tile_shape.restype = i32
-        lib.mpgemm_tile_shape.argtypes = [i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
-        lib.mpgemm_run_sp24.restype = i32
-        lib.mpgemm_run_sp24.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, i64, vp, i64, vp, i32,
-                                        i64, vp, vp, i32, i64, vp, i32, vp]
-        lib.mpgemm_check_sp24.restype = i32
-        lib.mpgemm_check_sp24.argtypes = [i32, i64, i64, i64, vp, vp, i32, i64, vp, i64, vp, i32,
-                                          i64, vp, vp, i32, i64, vp, i32]
-        u64 = ctypes.c_uint64
-        lib.mpgemm_run_bf16x3.restype = i32
-        lib.mpgemm_run_bf16x3.argtypes = [vp, i32, i32, i64, i64, i64, vp, vp, i64, vp, i64, vp,
-                                          vp, i64, vp, vp, u64, vp]
-        lib.mpgemm_bf16x3_workspace_size.restype = u64
-        lib.mpgemm_bf16x3_workspace_size.argtypes = [i32, i32, i64, i64, i64]
-        _lib = lib
+        _lib = declare(ctypes.CDLL(LIB_PATH))
     return _lib
 
 
@@ -190,6 +195,15 @@ def mpgemm_check_sp24(transb, m, n, k, alpha, Ac, a_type, lda, meta, ld_meta, B,
                                     _dtype(a_type), lda, _ptr(meta), ld_meta, _ptr(B),
                                     _dtype(b_type), ldb, ctypes.byref(be), _ptr(C), _dtype(c_type),
                                     ldc, _ptr(D), ct)
+
+
+def mpgemm_check_bf16x3(transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, D,
+                        workspace, workspace_bytes) -> int:
+    """Host-only argument check of mpgemm_run_bf16x3 (the workspace included)."""
+    al, be = ctypes.c_float(float(alpha)), ctypes.c_float(float(beta))
+    return load().mpgemm_check_bf16x3(_op(transa), _op(transb), m, n, k, ctypes.byref(al),
+                                      _ptr(A), lda, _ptr(B), ldb, ctypes.byref(be), _ptr(C), ldc,
+                                      _ptr(D), _ptr(workspace), int(workspace_bytes))
 
 
 def mpgemm_bf16x3_workspace_size(transa, transb, m: int, n: int, k: int) -> int:

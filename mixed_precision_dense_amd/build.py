@@ -1,7 +1,8 @@
 """Build the HIP library ``libmpgemm.so`` in-tree with hipcc for gfx950.
 
-Four translation units (the C-ABI host code and one kernel unit per input type) are compiled
-in parallel and linked into one shared library next to this file.
+The translation units (the C-ABI argument checks, the dispatch code, one kernel unit per input
+type or format pair, the split kernel of the three-product GEMM and the sparse kernels) are
+compiled in parallel and linked into one shared library next to this file.
 """
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmpgemm.so")
-SOURCES = ["mpgemm_api.hip", "kern_f16.hip", "kern_bf16.hip", "kern_i8.hip", "bf16x3.hip",
+SOURCES = ["mpgemm_host.cpp", "mpgemm_api.hip", "kern_f16.hip", "kern_bf16.hip", "kern_i8.hip", "bf16x3.hip",
            "kern_fp8_fp8.hip", "kern_fp8_bf8.hip", "kern_bf8_fp8.hip", "kern_bf8_bf8.hip",
            "sp24.hip", "sp24_fp8.hip"]
 ARCH = "gfx950"

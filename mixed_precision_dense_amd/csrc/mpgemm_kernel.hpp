@@ -57,6 +57,8 @@
 
 #include <utility>
 
+#include "mpgemm_kinds.hpp"
+
 namespace mpg {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -71,12 +73,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 typedef __attribute__((address_space(3))) char lds_char;
-
-// FP8 kinds name the A and B formats (OCP E4M3 "fp8", E5M2 "bf8").
-enum InKind { IN_F16 = 0, IN_BF16 = 1, IN_I8 = 2, IN_FP8_FP8 = 3, IN_FP8_BF8 = 4, IN_BF8_FP8 = 5,
-              IN_BF8_BF8 = 6 };
-constexpr bool is_fp8(int in) { return in >= IN_FP8_FP8 && in <= IN_BF8_BF8; }
-enum OutKind { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2, OUT_I32 = 3 };
 
 // Kernel arguments (one struct, passed by value).
 struct Params {
@@ -103,7 +99,6 @@ __device__ __forceinline__ void static_for(F &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-constexpr int kThreads = 256;
 constexpr int kStageKBytes = 128;   // bytes of k per row per stage (two MFMA k steps)
 constexpr int kStepKBytes = 64;     // bytes of k per row per MFMA k step
 constexpr int kSubTileBytes = 4096; // 32 rows x 128 B, or the transposed equivalent
@@ -896,7 +891,6 @@ hipError_t launch_bf8_fp8(int out, bool ta, bool tb, int tile, const Params &p, 
 hipError_t launch_bf8_bf8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
 // 2:4 structured-sparse A (sp24.hip, sp24_fp8.hip): A's kept values (m x k/2, lda) in Params::A, their
 // indices (2 bits per kept value, in k order; m rows of ld_meta bytes) in meta.
-constexpr int kSpTileM = 256, kSpTileN = 256;
 struct SpParams {
     Params p;
     const void *meta;

@@ -34,6 +34,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mpgemm_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libmpgemm_oracle.so")
+# A differently built copy of the same source (the sanitizer build of
+# tests/test_host_sanitizers.py) may be loaded in its place.
+_LIB_OVERRIDE = os.environ.get("MPGEMM_ORACLE_LIB")
 
 # Type codes private to the oracle (mirrors the enum in mpgemm_oracle.c).
 _CODES = {"f16": 0, "bf16": 1, "i8": 2, "f32": 3, "i32": 4, "e4m3": 5, "e5m2": 6}
@@ -59,9 +62,12 @@ _lib: Optional[ctypes.CDLL] = None
 def _load() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB_PATH)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB_PATH):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
         i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
         lib.oracle_decode.restype = dbl
         lib.oracle_decode.argtypes = [ctypes.c_uint64, i32, i32]

@@ -335,9 +335,10 @@ int oracle_num_threads(void) { return omp_get_max_threads(); }
  *                Inf x 0 and opposite infinities give NaN, other infinities propagate.
  *
  * The page leaves open the cut directions, the exponent a subnormal or zero operand stands
- * for, and overflow; the choices above are those that the GNFT-style vectors of
- * tests/mfma_numerics_probe.py find on gfx950's v_mfma_f32_16x16x32_{f16,bf16}, and so is
- * the sum width, which the page does not model.  With nblk = 8, frac = 24 (the 2+23+1
+ * for, and overflow; the choices above are those that GNFT-style feature-detection vectors
+ * find on gfx950's v_mfma_f32_16x16x32_{f16,bf16} (kept as GPU tests in
+ * tests/test_gpu_numerics.py and tests/test_gpu_bitexact.py), and so is the sum width, which
+ * the page does not model.  With nblk = 8, frac = 24 (the 2+23+1
  * accumulator) and sum_bits = 32 the model reproduces that instruction; other values give
  * the page's other models (V100: nblk = 4, frac = 22).
  *
@@ -485,7 +486,7 @@ static float mfma_block(float acc, const fp_parts *a, const fp_parts *b, int cnt
         if (sa > 64)
             return acc;   /* |products| < 2^(g + frac + 2 + 5) is below a quarter of acc's spacing */
         const i128 sM = acc < 0 ? -M : M;
-        S += sa >= 0 ? (sM << sa) : cut_floor(sM, -sa);
+        S += sa >= 0 ? sM * ((i128)1 << sa) : cut_floor(sM, -sa);   /* no shift of a negative */
     }
     if (sum_bits > 0 && S != 0) {
         /* keep sum_bits bits from the leading one, or from 2^-126 below FP32's normal range */

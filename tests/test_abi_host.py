@@ -111,6 +111,20 @@ def test_sizes_and_nulls():
                             P, 3, 8, P, 3) == ST["INVALID_VALUE"]    # bad transpose flag
 
 
+def test_size_limits():
+    """m and n up to 2^31 - 1; k up to 2^31 - 256, so that the kernel's stage count (k rounded
+    up to a whole stage, in 32-bit arithmetic) cannot overflow."""
+    big = (1 << 31) - 1
+    kmax = (1 << 31) - 256
+    # A stored k x m and B stored k x n: k is limited by neither leading dimension
+    tall = dict(transa=True, transb=False, m=1, n=1, lda=8, ldb=8, ldc=4)
+    assert chk(k=kmax, **tall) == ST["SUCCESS"]
+    assert chk(k=kmax + 1, **tall) == ST["NOT_SUPPORTED"]
+    assert chk(k=big, **tall) == ST["NOT_SUPPORTED"]
+    assert chk(k=big + 1, **tall) == ST["NOT_SUPPORTED"]
+    assert chk(m=big + 1) == ST["NOT_SUPPORTED"]
+
+
 def test_leading_dimension_minimums():
     assert chk(lda=56) == ST["INVALID_VALUE"]               # lda < k
     assert chk(transa=True, m=72, lda=64) == ST["INVALID_VALUE"]   # lda < m
@@ -156,6 +170,39 @@ def test_tile_shape():
     assert mp.mpgemm_tile_shape(2048, 2048) == (128, 128)   # 64 large tiles would idle 3/4 of the CUs
     assert mp.mpgemm_tile_shape(1024, 1024) == (64, 64)
     assert mp.mpgemm_tile_shape(1024, 1024, "e4m3") == (128, 128)
+
+
+def test_bf16x3_check():
+    """mpgemm_check_bf16x3 returns the status mpgemm_run_bf16x3 would return before any
+    device call, the workspace's size and alignment included."""
+    W = 1 << 24                                    # a 256-byte aligned fake workspace address
+
+    def c(**kw):
+        a = dict(transa=False, transb=True, m=64, n=64, k=64, alpha=1.0, A=P, lda=64, B=P,
+                 ldb=64, beta=0.0, C=None, ldc=64, D=P, workspace=W, workspace_bytes=None)
+        a.update(kw)
+        need = mp.mpgemm_bf16x3_workspace_size(a["transa"], a["transb"], a["m"], a["n"], a["k"])
+        wb = need if a["workspace_bytes"] is None else a["workspace_bytes"]
+        return mp.mpgemm_check_bf16x3(a["transa"], a["transb"], a["m"], a["n"], a["k"],
+                                      a["alpha"], a["A"], a["lda"], a["B"], a["ldb"], a["beta"],
+                                      a["C"], a["ldc"], a["D"], a["workspace"], wb)
+
+    assert c() == ST["SUCCESS"]
+    assert c(transa=True, transb=False, m=5, n=3, k=7, lda=8, ldb=4, ldc=4) == ST["SUCCESS"]
+    assert c(m=0, A=None, B=None, D=None, workspace=None) == ST["SUCCESS"]     # no-op
+    assert c(k=0, A=None, B=None, lda=4, workspace=None) == ST["SUCCESS"]      # D = beta C
+    assert c(workspace_bytes=1000) == ST["INVALID_VALUE"]                     # too small
+    assert c(workspace=None) == ST["INVALID_VALUE"]
+    assert c(workspace=W + 16) == ST["NOT_SUPPORTED"]                         # 256-byte alignment
+    assert c(m=-1) == ST["INVALID_VALUE"]
+    assert c(lda=60) == ST["INVALID_VALUE"]
+    assert c(lda=66) == ST["NOT_SUPPORTED"]                                   # 4-element strides
+    assert c(beta=1.0) == ST["INVALID_VALUE"]                                 # C needed
+    assert c(beta=1.0, C=P + 8) == ST["NOT_SUPPORTED"]                        # C misaligned
+    assert c(transa=True, transb=False, m=4, n=4, k=(1 << 31) // 3, lda=4, ldb=4,
+             ldc=4) == ST["NOT_SUPPORTED"]                                    # 3 kp past int32
+    assert mp.load().mpgemm_check_bf16x3(2, 0, 8, 8, 8, None, P, 8, P, 8, None, None, 8, P, W,
+                                         1 << 20) == ST["INVALID_VALUE"]
 
 
 def test_bf16x3_workspace_size():

@@ -154,35 +154,57 @@ def test_random_within_bound(in_type, out_type, ta, tb):
 
 
 # ----------------------------------------------------------------------------- the five workloads
+# Each configuration's whole output is compared with the oracle element by element (the
+# oracle's full pass takes about 2 s at 4096^3 and 20 s at 8192^3 on 16 host cores), and each
+# shape also runs once on integer-valued inputs, where every partial sum is exact in FP32 and
+# the output must equal the oracle bit for bit.
+def _int_valued(w, a_dist="int_uniform(-2,2)", c_dist=None, seed=None):
+    return Workload(w.name + "_int", w.in_type, w.out_type, w.m, w.n, w.k, transa=w.transa,
+                    transb=w.transb, alpha=w.alpha, beta=w.beta, a_dist=a_dist, b_dist=a_dist,
+                    c_dist=c_dist or w.c_dist, lda=w.lda, ldb=w.ldb, ldc=w.ldc,
+                    seed=w.seed if seed is None else seed)
+
+
 def test_workload_fp16_256_nn_beta1_full():
     rep, res = check_case(WORKLOADS["f16_256_nn_beta1"])
     _assert(rep, res)
     say(f"  worst error / bound = {rep.worst_ratio:.4f}")
 
 
-def test_workload_fp16_4096_nt_sampled():
-    rep, res = check_case(WORKLOADS["f16_4096_nt"], sample=3000)
+def test_workload_fp16_256_nn_beta1_exact_integer_valued():
+    w = _int_valued(WORKLOADS["f16_256_nn_beta1"], "int_uniform(-8,8)", "int_uniform(-100,100)")
+    rep, res = check_case(w, exact=True)
+    _assert(rep, res)
+
+
+def test_workload_fp16_4096_nt_full():
+    rep, res = check_case(WORKLOADS["f16_4096_nt"])
     _assert(rep, res)
     say(f"  worst error / bound = {rep.worst_ratio:.4f}")
 
 
 def test_workload_fp16_4096_nt_exact_integer_valued():
-    w = WORKLOADS["f16_4096_nt"]
-    w = Workload(w.name + "_int", w.in_type, w.out_type, w.m, w.n, w.k, transa=w.transa,
-                 transb=w.transb, a_dist="int_uniform(-2,2)", b_dist="int_uniform(-2,2)", seed=w.seed)
-    rep, res = check_case(w, exact=True, sample=3000)
+    rep, res = check_case(_int_valued(WORKLOADS["f16_4096_nt"]), exact=True)
     _assert(rep, res)
 
 
-def test_workload_bf16_8192_nn_sampled():
-    rep, res = check_case(WORKLOADS["bf16_8192_nn"], sample=1500)
+def test_workload_bf16_8192_nn_full():
+    rep, res = check_case(WORKLOADS["bf16_8192_nn"])
     _assert(rep, res)
     say(f"  worst error / bound = {rep.worst_ratio:.4f}")
 
 
-def test_workload_int8_4096_nn_sampled_and_in_place_beta1():
+def test_workload_bf16_8192_nn_exact_integer_valued():
+    """Integers in [-2, 2] for A and B and in [-64, 64] for C with beta = 0.5: |sum| <= 2^15
+    and beta * c is exact, so every partial sum and the epilogue are exact in FP32."""
+    w = _int_valued(WORKLOADS["bf16_8192_nn"], "int_uniform(-2,2)", "int_uniform(-64,64)")
+    rep, res = check_case(w, exact=True)
+    _assert(rep, res)
+
+
+def test_workload_int8_4096_nn_full_and_in_place_beta1():
     w = WORKLOADS["i8_4096_nn"]
-    rep, res = check_case(w, sample=4000)
+    rep, res = check_case(w)
     _assert(rep, res)
     # beta = 1 with C = 0 and D written over C in place: identical bits
     w1 = Workload(w.name + "_beta1", w.in_type, w.out_type, w.m, w.n, w.k, alpha=1, beta=1,
@@ -193,18 +215,16 @@ def test_workload_int8_4096_nn_sampled_and_in_place_beta1():
     assert res1.guard_ok
 
 
-def test_workload_fp16_ragged_f16out_sampled():
-    for name in ("f16_5000x3000x1000_f16out", "f16_5000x3000x1000_f16out_padded"):
-        rep, res = check_case(WORKLOADS[name], sample=4000)
-        _assert(rep, res)
-        say(f"  {name}: worst error / bound = {rep.worst_ratio:.4f}")
+@pytest.mark.parametrize("name", ["f16_5000x3000x1000_f16out", "f16_5000x3000x1000_f16out_padded"])
+def test_workload_fp16_ragged_f16out_full(name):
+    rep, res = check_case(WORKLOADS[name])
+    _assert(rep, res)
+    say(f"  {name}: worst error / bound = {rep.worst_ratio:.4f}")
 
 
-def test_workload_fp16_ragged_exact_full():
-    w = WORKLOADS["f16_5000x3000x1000_f16out_padded"]
-    w = Workload(w.name + "_int", "f16", "f16", w.m, w.n, w.k, a_dist="int_uniform(-2,2)",
-                 b_dist="int_uniform(-2,2)", lda=w.lda, ldb=w.ldb, ldc=w.ldc, seed=5)
-    rep, res = check_case(w, exact=True, sample=20000)
+@pytest.mark.parametrize("name", ["f16_5000x3000x1000_f16out", "f16_5000x3000x1000_f16out_padded"])
+def test_workload_fp16_ragged_exact_full(name):
+    rep, res = check_case(_int_valued(WORKLOADS[name], seed=5), exact=True)
     _assert(rep, res)
 
 
@@ -293,14 +313,14 @@ def test_error_left_pending_by_the_caller_does_not_fail_the_launch():
 def test_largest_accepted_strides_mn_contiguous(in_type, out_type):
     """A stored k x m and B stored k x n at the largest leading dimension the argument check
     accepts (256 rows just under 2 GiB), on 256 x 256 tiles: every offset of the 32-bit buffer
-    addressing within a stage stays in range (exact small integers, sampled outputs)."""
+    addressing within a stage stays in range (exact small integers, the whole output)."""
     eb = 2 if in_type == "f16" else 1
     ld = ((1 << 31) - 4096) // (256 * eb)
     assert (ld * eb) % 16 == 0
     w = Workload(f"maxld_{in_type}", in_type, out_type, 4096, 3072, 128, transa=True,
                  lda=ld, ldb=ld, a_dist="int_uniform(-3,3)", b_dist="int_uniform(-3,3)",
                  seed=57)
-    rep, res = check_case(w, exact=True, sample=20000)
+    rep, res = check_case(w, exact=True)
     _assert(rep, res)
 
 
@@ -335,11 +355,11 @@ def test_column_major_caller_through_the_operand_swap(dist, exact):
 @pytest.mark.parametrize("n", [2560, 3072])
 def test_shapes_on_one_partial_round_of_large_tiles(n):
     """Squares that the tile rule puts on one round of 256 x 256 tiles with part of the chip
-    idle (100 and 144 workgroups): exact integer inputs, sampled outputs against the oracle."""
+    idle (100 and 144 workgroups): exact integer inputs, the whole output against the oracle."""
     assert mp.mpgemm_tile_shape(n, n, "f16") == (256, 256)
     w = Workload(f"round_{n}", "f16", "f32", n, n, n, transb=True, a_dist="int_uniform(-2,2)",
                  b_dist="int_uniform(-2,2)", seed=60)
-    rep, res = check_case(w, exact=True, sample=20000)
+    rep, res = check_case(w, exact=True)
     _assert(rep, res)
 
 
