@@ -31,7 +31,10 @@
  *   a_type = b_type = MPGEMM_R_8I,   compute MPGEMM_R_32I, c_type MPGEMM_R_32I
  *   a_type, b_type each MPGEMM_R_8F_E4M3 or MPGEMM_R_8F_E5M2 (either pairing; the two FP8
  *     formats of "NVIDIA Tensor Core mixed-precision computing: principles and applications",
- *     section 4.3.1), compute MPGEMM_R_32F, c_type MPGEMM_R_32F or MPGEMM_R_16BF
+ *     section 4.3.1), compute MPGEMM_R_32F, c_type MPGEMM_R_32F or MPGEMM_R_16BF; here
+ *     "compute MPGEMM_R_32F" means an FP32 accumulator between 128-deep instructions only:
+ *     the sums inside each instruction keep about 13 bits (see below), so FP8 results are
+ *     not FP32-accurate sums of the products
  * FP16/BF16 outputs are rounded once from the FP32 result, to nearest with ties to even.
  * INT32 accumulation and the epilogue wrap modulo 2^32.
  *

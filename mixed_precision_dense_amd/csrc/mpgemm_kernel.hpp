@@ -430,6 +430,9 @@ __device__ __forceinline__ void drain_mfma(Acc (&acc)[FM][FN]) {
 template <int OUT> struct Out;
 template <> struct Out<OUT_F32> {
     static constexpr int kBytes = 4;
+    static __device__ __forceinline__ float lds_load(const lds_char *q) {
+        return *(const __attribute__((address_space(3))) float *)q;
+    }
     static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
     }
@@ -439,6 +442,9 @@ template <> struct Out<OUT_F32> {
 };
 template <> struct Out<OUT_F16> {
     static constexpr int kBytes = 2;
+    static __device__ __forceinline__ float lds_load(const lds_char *q) {
+        return (float)*(const __attribute__((address_space(3))) _Float16 *)q;
+    }
     static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
     }
@@ -452,6 +458,10 @@ template <> struct Out<OUT_F16> {
 };
 template <> struct Out<OUT_BF16> {
     static constexpr int kBytes = 2;
+    static __device__ __forceinline__ float lds_load(const lds_char *q) {
+        const uint32_t h = *(const __attribute__((address_space(3))) unsigned short *)q;
+        return __builtin_bit_cast(float, h << 16);
+    }
     static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
         return __builtin_bit_cast(float, h << 16);
@@ -463,6 +473,9 @@ template <> struct Out<OUT_BF16> {
 };
 template <> struct Out<OUT_I32> {
     static constexpr int kBytes = 4;
+    static __device__ __forceinline__ int lds_load(const lds_char *q) {
+        return *(const __attribute__((address_space(3))) int *)q;
+    }
     static __device__ __forceinline__ int load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
     }
@@ -494,10 +507,9 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 // arithmetic (INT8 inputs), else FP32 (see Out<>).  The 2 x 2 waves each hold FM x FN 16 x 16
 // blocks of a BM x BN tile.
 // ---------------------------------------------------------------------------------------
-template <bool kInt, int OUT, int FM, int FN, int BM, int BN, typename AccT>
+template <bool kInt, int OUT, int FM, int FN, int BM, int BN, bool kFull, typename AccT>
 __device__ __forceinline__ void store_tile(const Params &p, AccT (&acc)[FM][FN], int m0, int n0,
-                                           int wm, int wn, int lane, bool full_mn, int m_left,
-                                           int n_left) {
+                                           int wm, int wn, int lane, int m_left, int n_left) {
     constexpr int OB = Out<OUT>::kBytes;
     const int64_t tile_off = ((int64_t)m0 * p.ldc + n0) * OB;
     const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.D + tile_off);
@@ -510,8 +522,9 @@ __device__ __forceinline__ void store_tile(const Params &p, AccT (&acc)[FM][FN],
     auto out_off = [&](int i, int j, int r) -> uint32_t {
         const int row = row_base + i * 16 + r;
         const int col = col_base + j * 16;
-        const bool ok = full_mn || (row < m_left && col < n_left);
-        return ok ? (uint32_t)row * ldc_b + (uint32_t)col * OB : kOobOffset;
+        const uint32_t off = (uint32_t)row * ldc_b + (uint32_t)col * OB;
+        if constexpr (kFull) return off;
+        return ((row < m_left) & (col < n_left)) ? off : kOobOffset;
     };
     if (p.read_c) {
 #pragma unroll
@@ -547,6 +560,128 @@ __device__ __forceinline__ void store_tile(const Params &p, AccT (&acc)[FM][FN],
                         Out<OUT>::store(rd, out_off(i, j, r), p.alpha_f * acc[i][j][r]);
                 }
     }
+}
+
+// ---------------------------------------------------------------------------------------
+// Epilogue of one tile when C is read (beta != 0): the arithmetic of store_tile, with C
+// streamed through the LDS (free once the K loop is over: the caller has passed a barrier
+// after every wave's last loads and fragment reads) so that its loads are issued well ahead
+// of their use instead of block by block.  Each wave owns a quarter of the LDS as kSlots
+// slots of one block row (16 rows of its sub-tile): direct-to-LDS loads of whole 16-byte
+// chunks fill the slots ahead, and a slot is refilled with the block row kSlots further on as
+// soon as its values have been read.  Vector-memory operations of a wave complete in order,
+// so the wait for a block row counts the loads and stores issued after it.  Within a slot
+// the chunks of row rho sit at chunk position c ^ swz(rho), so that the four rows one
+// accumulator read touches fall on different LDS banks.  Chunks outside m x n are not read
+// (out-of-range offsets give zeros) and the elements they would feed are not stored.
+// ---------------------------------------------------------------------------------------
+// Number of vector-memory operations issued after the C loads of block row i, up to its wait:
+// loads of block rows 0 .. S-1 first, then per block row t its St stores followed by the loads
+// of block row t + S (L per block row).
+constexpr int c_ops_after(int i, int S, int FM, int L, int St) {
+    int pos = 0, done_i = -1;
+    for (int t = 0; t < S && t < FM; ++t) {
+        pos += L;
+        if (t == i) done_i = pos;
+    }
+    for (int t = 0; t < FM; ++t) {
+        if (t == i) return pos - done_i;
+        pos += St;
+        if (t + S < FM) {
+            pos += L;
+            if (t + S == i) done_i = pos;
+        }
+    }
+    return 0;
+}
+
+template <bool kInt, int OUT, int FM, int FN, int BM, int BN, int kRegionBytes, bool kFull,
+          typename AccT>
+__device__ __forceinline__ void store_tile_c_staged(const Params &p, AccT (&acc)[FM][FN], int m0,
+                                                    int n0, int wm, int wn, int lane, int m_left,
+                                                    int n_left, const lds_char *region,
+                                                    uint32_t region_addr) {
+    constexpr int OB = Out<OUT>::kBytes;
+    constexpr int WR = BM / 2, WC = BN / 2;                 // the wave's sub-tile
+    constexpr int RB = WC * OB;                             // bytes of one sub-tile row
+    constexpr int kCPR = RB / 16;                           // 16-byte chunks per row
+    constexpr int kSlotBytes = 16 * RB;                     // one block row
+    constexpr int L = kSlotBytes / 1024;                    // 1 KB direct loads per block row
+    constexpr int S = kRegionBytes / kSlotBytes < FM ? kRegionBytes / kSlotBytes : FM;
+    constexpr int St = FN * 4;                              // stores per block row
+    static_assert(RB >= 16 && kSlotBytes % 1024 == 0 && S >= 1, "C staging geometry");
+    static_assert(WR == 16 * FM, "sub-tile rows");
+    using CT = decltype(Out<OUT>::lds_load(nullptr));   // float, or int for INT32 C
+
+    const int64_t tile_off = ((int64_t)m0 * p.ldc + n0) * OB;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.D + tile_off);
+    const i32x4 rc_words = make_rsrc_words((const char *)p.C + tile_off);
+    const uint32_t ldc_b = (uint32_t)(p.ldc * OB);
+    const int row0 = wm * WR, col0 = wn * WC;               // sub-tile origin within the tile
+    auto swz = [](int rho) { return (((rho & 15) >> 2) * OB) & (kCPR - 1); };
+
+    // Lane l of load q of a block row fills slot bytes q KB + 16 l: row rho, physical chunk
+    // cp, which holds logical chunk cp ^ swz(rho).
+    auto load_block_row = [&](int i, int slot) {
+#pragma unroll
+        for (int q = 0; q < L; ++q) {
+            const int pos = q * 1024 + 16 * lane;
+            const int rho = pos / RB;
+            const int c = ((pos % RB) / 16) ^ swz(rho);
+            const int row = row0 + 16 * i + rho;
+            const int col = col0 + c * (16 / OB);
+            uint32_t voff = (uint32_t)row * ldc_b + (uint32_t)col * OB;
+            if constexpr (!kFull) voff = ((row < m_left) & (col < n_left)) ? voff : kOobOffset;
+            dma16(rc_words, voff, 0u, region_addr + (uint32_t)(slot * kSlotBytes + q * 1024));
+        }
+    };
+    // accumulator register r of block (i, j): row 16 i + 4 (lane / 16) + r, column 16 j + lane % 16
+    const int g = lane / 16, u = lane % 16;
+    const int row_base = row0 + 4 * g;
+    const int col_base = col0 + u;
+    auto out_off = [&](int i, int j, int r) -> uint32_t {
+        const int row = row_base + i * 16 + r;
+        const int col = col_base + j * 16;
+        const uint32_t off = (uint32_t)row * ldc_b + (uint32_t)col * OB;
+        if constexpr (kFull) return off;
+        return ((row < m_left) & (col < n_left)) ? off : kOobOffset;
+    };
+    // byte offset within a slot of this lane's element of row 4 g + r, block column j
+    auto c_at = [&](int j, int r) -> int {
+        const int colb = (16 * j + u) * OB;                 // byte column in the row
+        return (4 * g + r) * RB + ((((colb >> 4) ^ swz(4 * g + r))) << 4) + (colb & 15);
+    };
+
+    static_for<S>([&](auto t_c) { load_block_row(decltype(t_c)::value, decltype(t_c)::value); });
+    static_for<FM>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int after = c_ops_after(i, S, FM, L, St);
+        wait_vmem<(after < 63 ? after : 63)>();          // block row i's C is in its slot
+        const lds_char *slot = region + (i % S) * kSlotBytes;
+        CT cv[FN][4];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cv[j][r] = Out<OUT>::lds_load(slot + c_at(j, r));
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (kInt) {
+                    const uint32_t v = (uint32_t)p.alpha_i * (uint32_t)acc[i][j][r] +
+                                       (uint32_t)p.beta_i * (uint32_t)cv[j][r];
+                    Out<OUT>::store(rd, out_off(i, j, r), (int)v);
+                } else {
+                    // one rounding of beta * c, then alpha * acc + (beta * c) fused
+                    Out<OUT>::store(rd, out_off(i, j, r),
+                                    __builtin_fmaf(p.alpha_f, acc[i][j][r], p.beta_f * cv[j][r]));
+                }
+            }
+        if constexpr (i + S < FM) {
+            wait_lds<0>();                                  // the slot's values are in registers
+            load_block_row(i + S, i % S);
+        }
+    });
 }
 
 // ---------------------------------------------------------------------------------------
@@ -866,7 +1001,31 @@ void gemm_kernel(Params p) {
     drain_mfma(acc);
 
     // ---- epilogue
-    store_tile<IN == IN_I8, OUT, FM, FN, BM, BN>(p, acc, m0, n0, wm, wn, lane, full_mn, m_left, n_left);
+    // (full_mn, p.read_c and the wave index are uniform across a wave)
+    // The lane index passes through an empty statement here, so that the epilogue's per-lane
+    // addresses are computed after the loop rather than held in registers across it.
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    if (p.read_c) {
+        // every wave's loads and fragment reads are complete: the LDS is free for C
+        __syncthreads();
+        constexpr int kRegion = kBuffers * (A_BYTES + B_BYTES) / 4;   // LDS bytes per wave
+        const int w = __builtin_amdgcn_readfirstlane(wave);
+        const lds_char *region = smem + w * kRegion;
+        const uint32_t region_addr = (uint32_t)(uintptr_t)smem + (uint32_t)(w * kRegion);
+        if (full_mn)
+            store_tile_c_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, true>(
+                p, acc, m0, n0, wm, wn, lane_e, m_left, n_left, region, region_addr);
+        else
+            store_tile_c_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, false>(
+                p, acc, m0, n0, wm, wn, lane_e, m_left, n_left, region, region_addr);
+    } else if (full_mn) {
+        store_tile<IN == IN_I8, OUT, FM, FN, BM, BN, true>(p, acc, m0, n0, wm, wn, lane_e, m_left,
+                                                           n_left);
+    } else {
+        store_tile<IN == IN_I8, OUT, FM, FN, BM, BN, false>(p, acc, m0, n0, wm, wn, lane_e, m_left,
+                                                            n_left);
+    }
 }
 
 // Host-side launcher of one instance.  hipLaunchKernel returns this launch's own status (an
