@@ -108,8 +108,13 @@ typedef enum {
     MPGEMM_STATUS_NO_DEVICE = 5,       /* no HIP device, or the current device is not gfx950 */
     MPGEMM_STATUS_LAUNCH_FAILED = 6,   /* the kernel launch was rejected by the runtime */
     MPGEMM_STATUS_INTERNAL_ERROR = 7,
-    MPGEMM_STATUS_WRONG_DEVICE = 8     /* current device differs from the handle's device */
+    MPGEMM_STATUS_WRONG_DEVICE = 8,    /* current device differs from the handle's device */
+    MPGEMM_STATUS_SCRATCH_TOO_SMALL = 9 /* mpgemm_run_bf16x3_noalloc: the split operands need
+                                           more than MPGEMM_NOALLOC_SCRATCH_BYTES */
 } mpgemm_status_t;
+
+/* Size of the library's fixed scratch buffer (per device) used by mpgemm_run_bf16x3_noalloc. */
+#define MPGEMM_NOALLOC_SCRATCH_BYTES (64ull << 20)
 
 /* Create a handle bound to the current HIP device.  Returns MPGEMM_STATUS_NO_DEVICE when no
  * device is present or the device is not a gfx950, MPGEMM_STATUS_INVALID_VALUE when
@@ -170,6 +175,29 @@ mpgemm_status_t mpgemm_run_bf16x3(mpgemm_handle_t handle, mpgemm_op_t transa,
                                   const float *B, int64_t ldb, const float *beta,
                                   const float *C, int64_t ldc, float *D, void *workspace,
                                   uint64_t workspace_bytes, void *stream);
+
+/* mpgemm_run_bf16x3 without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results, with the split operands kept in a fixed device array of
+ * the library (MPGEMM_NOALLOC_SCRATCH_BYTES = 64 MiB per device, reserved when the library's
+ * code is first loaded on a device and held until the process ends) instead of a
+ * caller-provided workspace.  The call allocates nothing and frees nothing.
+ *   - Problems whose workspace, mpgemm_bf16x3_workspace_size(transa, transb, m, n, k),
+ *     exceeds MPGEMM_NOALLOC_SCRATCH_BYTES return MPGEMM_STATUS_SCRATCH_TOO_SMALL without
+ *     launching anything (for example m x k + k x n up to about 11 million elements fits).
+ *   - All calls on one device share that device's buffer, which keeps the last call's
+ *     contents: calls that may overlap on one device (different streams, handles or host
+ *     threads without ordering between them) race and give wrong results; calls ordered on
+ *     one stream are safe.  No byte of it needs to start at zero: each call writes every
+ *     byte its GEMM reads.
+ *   - Other arguments, ownership and errors as for mpgemm_run_bf16x3; the handle must have
+ *     been created on the current device (its creation looks the buffer's address up;
+ *     MPGEMM_STATUS_INTERNAL_ERROR if that failed). */
+mpgemm_status_t mpgemm_run_bf16x3_noalloc(mpgemm_handle_t handle, mpgemm_op_t transa,
+                                          mpgemm_op_t transb, int64_t m, int64_t n, int64_t k,
+                                          const float *alpha, const float *A, int64_t lda,
+                                          const float *B, int64_t ldb, const float *beta,
+                                          const float *C, int64_t ldc, float *D, void *stream);
 
 /* Host-only argument check of mpgemm_run_bf16x3: returns exactly the status mpgemm_run_bf16x3
  * would return for these arguments before touching the device (the workspace's size and

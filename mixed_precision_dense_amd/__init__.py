@@ -26,8 +26,9 @@ DTYPES = {"f16": R_16F, "bf16": R_16BF, "i8": R_8I, "f32": R_32F, "i32": R_32I,
           "e4m3": R_8F_E4M3, "e5m2": R_8F_E5M2}
 STATUS = {0: "SUCCESS", 1: "NOT_INITIALIZED", 2: "INVALID_VALUE", 3: "NOT_SUPPORTED",
           4: "ALLOC_FAILED", 5: "NO_DEVICE", 6: "LAUNCH_FAILED", 7: "INTERNAL_ERROR",
-          8: "WRONG_DEVICE"}
+          8: "WRONG_DEVICE", 9: "SCRATCH_TOO_SMALL"}
 SUCCESS = 0
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MPGEMM_NOALLOC_SCRATCH_BYTES
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -55,6 +56,8 @@ SIGNATURES = {
                                  _i32, _i64, _vp, _vp, _i32, _i64, _vp, _i32]),
     "mpgemm_run_bf16x3": (_i32, [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64,
                                  _vp, _vp, _i64, _vp, _vp, _u64, _vp]),
+    "mpgemm_run_bf16x3_noalloc": (_i32, [_vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp,
+                                         _i64, _vp, _vp, _i64, _vp, _vp]),
     "mpgemm_check_bf16x3": (_i32, [_i32, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
                                    _vp, _i64, _vp, _vp, _u64]),
     "mpgemm_bf16x3_workspace_size": (_u64, [_i32, _i32, _i64, _i64, _i64]),
@@ -167,6 +170,20 @@ def mpgemm_run_bf16x3(handle, transa, transb, m, n, k, alpha, A, lda, B, ldb, be
                                   _stream(stream))
     if check and st != SUCCESS:
         raise MpgemmError(st, "mpgemm_run_bf16x3")
+    return st
+
+
+def mpgemm_run_bf16x3_noalloc(handle, transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C,
+                              ldc, D, stream=None, check: bool = True) -> int:
+    """mpgemm_run_bf16x3 with the library's fixed scratch buffer in place of a workspace (no
+    allocation; calls that overlap on one device race)."""
+    al, be = ctypes.c_float(float(alpha)), ctypes.c_float(float(beta))
+    st = load().mpgemm_run_bf16x3_noalloc(handle, _op(transa), _op(transb), m, n, k,
+                                          ctypes.byref(al), _ptr(A), lda, _ptr(B), ldb,
+                                          ctypes.byref(be), _ptr(C), ldc, _ptr(D),
+                                          _stream(stream))
+    if check and st != SUCCESS:
+        raise MpgemmError(st, "mpgemm_run_bf16x3_noalloc")
     return st
 
 

@@ -3,6 +3,7 @@
 // are in mpgemm_host.cpp).  No device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <map>
 #include <mutex>
 #include <new>
 #include <set>
@@ -17,7 +18,16 @@ using namespace mpg_host;
 struct mpgemm_handle_s {
     int device;
     int num_cus;
+    void *scratch;   // this device's address of `scratch` (below), or nullptr
 };
+
+// Fixed scratch buffer of mpgemm_run_bf16x3_noalloc, for callers that cannot allocate: it
+// holds the BF16 pieces of the split operands, laid out as mpgemm_run_bf16x3's workspace.
+// Static device memory: every device the library runs on has its own copy, at its own
+// address, until the process ends; all calls on one device share it.  In host code the name
+// is only a stand-in for the symbol: kernels and copies use the address that
+// hipGetSymbolAddress returns for the current device (scratch_address).
+static __device__ __align__(256) unsigned char scratch[MPGEMM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -27,6 +37,24 @@ std::set<mpgemm_handle_t> g_handles;  // live handles; lets destroyed ones be re
 bool handle_live(mpgemm_handle_t h) {
     std::lock_guard<std::mutex> lock(g_handles_mu);
     return g_handles.count(h) != 0;
+}
+
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch_addr;   // device -> address of `scratch` on that device
+
+// Address of `scratch` on device `dev`, which must be the current device: looked up once per
+// device (hipGetSymbolAddress, at handle creation) and kept; nullptr if the lookup fails.
+void *scratch_address(int dev) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    const auto it = g_scratch_addr.find(dev);
+    if (it != g_scratch_addr.end()) return it->second;
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    g_scratch_addr[dev] = ptr;
+    return ptr;
 }
 
 }  // namespace
@@ -80,6 +108,25 @@ mpgemm_status_t mpgemm_run_bf16x3(mpgemm_handle_t handle, mpgemm_op_t transa,
                       stream);
 }
 
+mpgemm_status_t mpgemm_run_bf16x3_noalloc(mpgemm_handle_t handle, mpgemm_op_t transa,
+                                          mpgemm_op_t transb, int64_t m, int64_t n, int64_t k,
+                                          const float *alpha, const float *A, int64_t lda,
+                                          const float *B, int64_t ldb, const float *beta,
+                                          const float *C, int64_t ldc, float *D, void *stream) {
+    if (!handle || !handle_live(handle)) return MPGEMM_STATUS_NOT_INITIALIZED;
+    if (!handle->scratch) return MPGEMM_STATUS_INTERNAL_ERROR;   // lookup at creation failed
+    const uint64_t cap = MPGEMM_NOALLOC_SCRATCH_BYTES;
+    const uint64_t need = mpgemm_bf16x3_workspace_size(transa, transb, m, n, k);
+    // every other argument as mpgemm_run_bf16x3 checks it; then the scratch limit
+    const mpgemm_status_t st =
+        mpgemm_check_bf16x3(transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, D,
+                            handle->scratch, need > cap ? need : cap);
+    if (st != MPGEMM_STATUS_SUCCESS) return st;
+    if (need > cap) return MPGEMM_STATUS_SCRATCH_TOO_SMALL;
+    return mpgemm_run_bf16x3(handle, transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C,
+                             ldc, D, handle->scratch, cap, stream);
+}
+
 mpgemm_status_t mpgemm_create(mpgemm_handle_t *handle) {
     if (!handle) return MPGEMM_STATUS_INVALID_VALUE;
     *handle = nullptr;
@@ -97,6 +144,7 @@ mpgemm_status_t mpgemm_create(mpgemm_handle_t *handle) {
     if (!h) return MPGEMM_STATUS_ALLOC_FAILED;
     h->device = dev;
     h->num_cus = prop.multiProcessorCount;
+    h->scratch = scratch_address(dev);   // checked by mpgemm_run_bf16x3_noalloc
     {
         std::lock_guard<std::mutex> lock(g_handles_mu);
         g_handles.insert(h);

@@ -279,6 +279,7 @@ const char *mpgemm_status_string(mpgemm_status_t status) {
     case MPGEMM_STATUS_LAUNCH_FAILED: return "kernel launch failed";
     case MPGEMM_STATUS_INTERNAL_ERROR: return "internal error";
     case MPGEMM_STATUS_WRONG_DEVICE: return "current HIP device is not the handle's device";
+    case MPGEMM_STATUS_SCRATCH_TOO_SMALL: return "the problem needs more than the library's fixed 64 MiB scratch buffer";
     }
     return "unknown status";
 }

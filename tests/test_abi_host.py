@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(0, 9):
+    for code in range(0, 10):
         s = mp.status_string(code)
         assert isinstance(s, str) and len(s) > 3
     assert "unknown" in mp.status_string(99)
