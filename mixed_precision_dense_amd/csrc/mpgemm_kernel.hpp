@@ -188,12 +188,13 @@ __device__ __forceinline__ u32x4 keep_first_bytes(u32x4 v, int nbytes) {
 // beyond K within a row are the exception -- they would reach every output -- and are zeroed
 // in LDS once they have landed (fix_k_tail).
 // ---------------------------------------------------------------------------------------
-template <int EB, bool KC, int NS>
+template <int EB, bool KC, int NS, int R = 1>
 struct Operand {
     static_assert(NS == 2 || NS == 4 || NS == 8, "sub-tile count");
+    static_assert((R == 1 || R == 2) && NS % R == 0, "waves per quarter slot");
     static constexpr int kStageBytes = NS * kSubTileBytes;
     static constexpr int kChunkElems = 16 / EB;             // elements per 16-byte chunk
-    static constexpr int kSlots = NS;                       // 1 KB loads per wave per stage
+    static constexpr int kSlots = NS / R;                   // 1 KB loads per wave per stage
     static constexpr int kStageK = kStageKBytes / EB;       // k elements per stage
     static constexpr int kStepK = kStepKBytes / EB;         // k elements per MFMA k step
     // MN-contiguous geometry: k-rows of 128-byte column groups, kGroupBlocks 16-wide fragment
@@ -204,13 +205,13 @@ struct Operand {
     static constexpr int kSlotsPerGroup = kStageK / 32;     // 2 (16-bit) or 4 (8-bit)
     static_assert(KC || 2 * NS >= kGroupBlocks, "transposed operand needs whole column groups");
 
-    // Load slot i of wave w writes 1 KB at i * 4096 + w * 1024 of the operand's stage, lane l
-    // the 16 bytes at l * 16: for a K-contiguous operand quarter w of sub-tile i (8 rows x
-    // 128 B), for an MN-contiguous one rows 32 (i % kSlotsPerGroup) + 8 w .. + 7 of column
-    // group i / kSlotsPerGroup.
+    // The stage is cut into 1 KB quarters, four per 4 KB sub-tile position o (0 .. NS - 1);
+    // quarter v of position o sits at o * 4096 + v * 1024, lane l's 16 bytes at l * 16: for a
+    // K-contiguous operand quarter v of sub-tile o (8 rows x 128 B), for an MN-contiguous one
+    // rows 32 (o % kSlotsPerGroup) + 8 v .. + 7 of column group o / kSlotsPerGroup.  With 4R
+    // waves, wave w loads quarter v = w % 4 of the positions o = i R + w / 4, its slots
+    // i = 0 .. kSlots - 1.
     uint32_t voff[kSlots];  // per slot: byte offset of this lane's chunk from the stage start
-    uint32_t l_off0;        // LDS byte offset of this lane's slot-0 chunk within the stage
-    int k0_idx;             // K-contig: k index (within the stage) of this lane's chunks
     // fragment read offsets: K-contig per k step; MN-contig per block position in its group
     uint32_t r_off[kGroupBlocks > 2 ? kGroupBlocks : 2];
 
@@ -231,16 +232,17 @@ struct Operand {
     // mn_left: rows (K-contig) or columns (MN-contig) of the operand from the tile's first
     // one; at least 1.
     // lds_base: byte offset of this operand's stages in LDS, folded into the read offsets.
-    __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int mn_left, uint32_t lds_base) {
+    // wave: the quarter v this wave loads (wave index mod 4); hi: the wave index / 4.
+    __device__ __forceinline__ void init(int wave, int hi, int lane, int64_t ld, int mn_left,
+                                         uint32_t lds_base) {
         const uint32_t row_bytes = (uint32_t)(ld * EB);
-        l_off0 = (uint32_t)(wave * 1024 + lane * 16);
         const int g = lane / 16, u = lane % 16;
         if constexpr (KC) {
             const int r = wave * 8 + lane / 8;                      // row within the sub-tile
             const int c = (lane % 8) ^ kc_swz(r);                   // logical chunk of phys lane % 8
-            k0_idx = c * kChunkElems;
 #pragma unroll
-            for (int i = 0; i < kSlots; ++i) voff[i] = (uint32_t)min(32 * i + r, mn_left - 1) * row_bytes + 16u * c;
+            for (int i = 0; i < kSlots; ++i)
+                voff[i] = (uint32_t)min(32 * (i * R + hi) + r, mn_left - 1) * row_bytes + 16u * c;
             // fragment: lane reads row u of its 16-row block, chunk g of the 64-byte k step
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
@@ -248,14 +250,15 @@ struct Operand {
         } else {
             const int kr = wave * 8 + lane / 8;                     // k-row within a 32-row slot
             const int c = (lane % 8) ^ mn_swz(kr);                  // logical chunk in the group
-            k0_idx = kr;
             // chunks past the operand's row end (edge tiles) are clamped to its last 16-byte
             // block, so no load runs into later rows
             const int col_max = ((mn_left * EB + 15) & ~15) - 16;
 #pragma unroll
-            for (int i = 0; i < kSlots; ++i)
-                voff[i] = (uint32_t)(32 * (i % kSlotsPerGroup) + kr) * row_bytes +
-                          (uint32_t)min((i / kSlotsPerGroup) * 128 + 16 * c, col_max);
+            for (int i = 0; i < kSlots; ++i) {
+                const int o = i * R + hi;                           // sub-tile position
+                voff[i] = (uint32_t)(32 * (o % kSlotsPerGroup) + kr) * row_bytes +
+                          (uint32_t)min((o / kSlotsPerGroup) * 128 + 16 * c, col_max);
+            }
             if constexpr (EB == 2) {
                 // tr16: lane 4 s + q of group g reads k-row 8 g + s (+4 for the high half),
                 // 8 bytes at column 4 q of its 16-column block
@@ -275,23 +278,31 @@ struct Operand {
     }
 
     // Queue load slot i of a stage: rs addresses the stage's start (record count bounded as
-    // described above), lds_stage_w is the LDS address of the stage plus 1024 * wave.
+    // described above), lds_stage_w is the LDS address of the stage plus this wave's
+    // 4096 * hi + 1024 * wave.
     __device__ __forceinline__ void load(i32x4 rs, uint32_t lds_stage_w, int i) const {
-        dma16(rs, voff[i], 0u, lds_stage_w + (uint32_t)i * 4096u);
+        dma16(rs, voff[i], 0u, lds_stage_w + (uint32_t)(i * R) * 4096u);
     }
 
     // After the last stage has landed, when K ends inside it: zero this lane's K-contiguous
     // chunks at and past K (whole chunks past K, the tail of the chunk that straddles it).
-    // MN-contiguous k-rows past K lie beyond the operand and were read as zeros.
-    __device__ __forceinline__ void fix_k_tail(lds_char *stage, int k_left) const {
+    // MN-contiguous k-rows past K lie beyond the operand and were read as zeros.  The lane's
+    // chunk position is recomputed here (from an opaque copy of the lane index), so that none
+    // of it is held in registers across the K loop.
+    __device__ __forceinline__ void fix_k_tail(lds_char *stage, int k_left, int wave, int hi,
+                                               int lane) const {
         if constexpr (KC) {
-            const int kvalid = k_left - k0_idx;
+            asm volatile("" : "+v"(lane));
+            const int r = wave * 8 + lane / 8;
+            const int k0 = ((lane % 8) ^ kc_swz(r)) * kChunkElems;   // first k of its chunks
+            const uint32_t l_off = (uint32_t)(hi * 4096 + wave * 1024 + lane * 16);
+            const int kvalid = k_left - k0;
             if (kvalid < kChunkElems) {
                 const int keep = kvalid > 0 ? kvalid * EB : 0;
 #pragma unroll
                 for (int i = 0; i < kSlots; ++i) {
                     typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-                    lds_u32x4 *q = (lds_u32x4 *)(stage + i * 4096 + l_off0);
+                    lds_u32x4 *q = (lds_u32x4 *)(stage + i * R * 4096 + l_off);
                     *q = keep_first_bytes(*q, keep);
                 }
             }
@@ -433,6 +444,9 @@ template <> struct Out<OUT_F32> {
     static __device__ __forceinline__ float lds_load(const lds_char *q) {
         return *(const __attribute__((address_space(3))) float *)q;
     }
+    static __device__ __forceinline__ void lds_store(lds_char *q, float v) {
+        *(__attribute__((address_space(3))) float *)q = v;
+    }
     static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
     }
@@ -444,6 +458,10 @@ template <> struct Out<OUT_F16> {
     static constexpr int kBytes = 2;
     static __device__ __forceinline__ float lds_load(const lds_char *q) {
         return (float)*(const __attribute__((address_space(3))) _Float16 *)q;
+    }
+    static __device__ __forceinline__ void lds_store(lds_char *q, float v) {
+        asm("" : "+v"(v));   // the FP32 value, then one RNE conversion (see store)
+        *(__attribute__((address_space(3))) _Float16 *)q = (_Float16)v;
     }
     static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
@@ -462,6 +480,10 @@ template <> struct Out<OUT_BF16> {
         const uint32_t h = *(const __attribute__((address_space(3))) unsigned short *)q;
         return __builtin_bit_cast(float, h << 16);
     }
+    static __device__ __forceinline__ void lds_store(lds_char *q, float v) {
+        *(__attribute__((address_space(3))) unsigned short *)q =
+            __builtin_bit_cast(unsigned short, (__bf16)v);
+    }
     static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
         return __builtin_bit_cast(float, h << 16);
@@ -475,6 +497,9 @@ template <> struct Out<OUT_I32> {
     static constexpr int kBytes = 4;
     static __device__ __forceinline__ int lds_load(const lds_char *q) {
         return *(const __attribute__((address_space(3))) int *)q;
+    }
+    static __device__ __forceinline__ void lds_store(lds_char *q, int v) {
+        *(__attribute__((address_space(3))) int *)q = v;
     }
     static __device__ __forceinline__ int load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
@@ -504,10 +529,11 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 
 // ---------------------------------------------------------------------------------------
 // Epilogue of one tile: D = alpha * acc + beta * C, masked to m x n.  kInt: INT32 wrap-around
-// arithmetic (INT8 inputs), else FP32 (see Out<>).  The 2 x 2 waves each hold FM x FN 16 x 16
-// blocks of a BM x BN tile.
+// arithmetic (INT8 inputs), else FP32 (see Out<>).  The 2 x (NW / 2) waves each hold FM x FN
+// 16 x 16 blocks of a BM x BN tile.
 // ---------------------------------------------------------------------------------------
-template <bool kInt, int OUT, int FM, int FN, int BM, int BN, bool kFull, typename AccT>
+template <bool kInt, int OUT, int FM, int FN, int BM, int BN, bool kFull, int NW = 4,
+          typename AccT>
 __device__ __forceinline__ void store_tile(const Params &p, AccT (&acc)[FM][FN], int m0, int n0,
                                            int wm, int wn, int lane, int m_left, int n_left) {
     constexpr int OB = Out<OUT>::kBytes;
@@ -517,7 +543,7 @@ __device__ __forceinline__ void store_tile(const Params &p, AccT (&acc)[FM][FN],
     const uint32_t ldc_b = (uint32_t)(p.ldc * OB);
     // accumulator register r of block (i, j): row 16 i + 4 (lane / 16) + r, column 16 j + lane % 16
     const int row_base = wm * (BM / 2) + 4 * (lane / 16);
-    const int col_base = wn * (BN / 2) + (lane % 16);
+    const int col_base = wn * (BN / (NW / 2)) + (lane % 16);
     // byte offset of accumulator element r of block (i, j), or an out-of-range offset
     auto out_off = [&](int i, int j, int r) -> uint32_t {
         const int row = row_base + i * 16 + r;
@@ -596,13 +622,13 @@ constexpr int c_ops_after(int i, int S, int FM, int L, int St) {
 }
 
 template <bool kInt, int OUT, int FM, int FN, int BM, int BN, int kRegionBytes, bool kFull,
-          typename AccT>
+          int NW, typename AccT>
 __device__ __forceinline__ void store_tile_c_staged(const Params &p, AccT (&acc)[FM][FN], int m0,
                                                     int n0, int wm, int wn, int lane, int m_left,
                                                     int n_left, const lds_char *region,
                                                     uint32_t region_addr) {
     constexpr int OB = Out<OUT>::kBytes;
-    constexpr int WR = BM / 2, WC = BN / 2;                 // the wave's sub-tile
+    constexpr int WR = BM / 2, WC = BN / (NW / 2);          // the wave's sub-tile
     constexpr int RB = WC * OB;                             // bytes of one sub-tile row
     constexpr int kCPR = RB / 16;                           // 16-byte chunks per row
     constexpr int kSlotBytes = 16 * RB;                     // one block row
@@ -610,7 +636,7 @@ __device__ __forceinline__ void store_tile_c_staged(const Params &p, AccT (&acc)
     constexpr int S = kRegionBytes / kSlotBytes < FM ? kRegionBytes / kSlotBytes : FM;
     constexpr int St = FN * 4;                              // stores per block row
     static_assert(RB >= 16 && kSlotBytes % 1024 == 0 && S >= 1, "C staging geometry");
-    static_assert(WR == 16 * FM, "sub-tile rows");
+    static_assert(WR == 16 * FM && WC == 16 * FN, "sub-tile shape");
     using CT = decltype(Out<OUT>::lds_load(nullptr));   // float, or int for INT32 C
 
     const int64_t tile_off = ((int64_t)m0 * p.ldc + n0) * OB;
@@ -685,18 +711,118 @@ __device__ __forceinline__ void store_tile_c_staged(const Params &p, AccT (&acc)
 }
 
 // ---------------------------------------------------------------------------------------
-// The kernel
+// Epilogue of a whole tile (no edge) through the LDS: the same arithmetic as store_tile (and,
+// with kReadC, C streamed through the slots as in store_tile_c_staged), but each wave writes
+// its block row of results into its slot in the row-major, chunk-swizzled layout and stores
+// it to D by whole 16-byte chunks, row by row (a 1 KB store instruction covers two to eight
+// full rows of the sub-tile instead of four 64- or 32-byte pieces of sixteen rows).  The
+// caller has passed a barrier after every wave's last loads and fragment reads.
 // ---------------------------------------------------------------------------------------
-template <int IN, int OUT, bool TA, bool TB, int BM, int BN>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-void gemm_kernel(Params p) {
+template <bool kInt, int OUT, int FM, int FN, int BM, int BN, int kRegionBytes, int NW,
+          bool kReadC, typename AccT>
+__device__ __forceinline__ void store_full_tile_staged(const Params &p, AccT (&acc)[FM][FN],
+                                                       int m0, int n0, int wm, int wn, int lane,
+                                                       lds_char *region, uint32_t region_addr) {
+    constexpr int OB = Out<OUT>::kBytes;
+    constexpr int WR = BM / 2, WC = BN / (NW / 2);          // the wave's sub-tile
+    constexpr int RB = WC * OB;                             // bytes of one sub-tile row
+    constexpr int kCPR = RB / 16;                           // 16-byte chunks per row
+    constexpr int kSlotBytes = 16 * RB;                     // one block row
+    constexpr int L = kSlotBytes / 1024;                    // 1 KB loads (stores) per block row
+    constexpr int S = kRegionBytes / kSlotBytes < FM ? kRegionBytes / kSlotBytes : FM;
+    static_assert(RB >= 16 && kSlotBytes % 1024 == 0 && S >= 1, "staging geometry");
+    static_assert(WR == 16 * FM && WC == 16 * FN, "sub-tile shape");
+    using CT = decltype(Out<OUT>::lds_load(nullptr));   // float, or int for INT32 C
+
+    const int64_t tile_off = ((int64_t)m0 * p.ldc + n0) * OB;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.D + tile_off);
+    const i32x4 rc_words = make_rsrc_words((const char *)(kReadC ? p.C : p.D) + tile_off);
+    const uint32_t ldc_b = (uint32_t)(p.ldc * OB);
+    const int row0 = wm * WR, col0 = wn * WC;               // sub-tile origin within the tile
+    auto swz = [](int rho) { return (((rho & 15) >> 2) * OB) & (kCPR - 1); };
+    // Byte offset in D (from the tile's origin) of the chunk at slot bytes q KB + 16 lane of
+    // block row i: row rho, physical chunk cp, holding logical chunk cp ^ swz(rho).
+    auto chunk_off = [&](int i, int q) -> uint32_t {
+        const int pos = q * 1024 + 16 * lane;
+        const int rho = pos / RB;
+        const int c = ((pos % RB) / 16) ^ swz(rho);
+        return (uint32_t)(row0 + 16 * i + rho) * ldc_b + (uint32_t)(col0 + c * (16 / OB)) * OB;
+    };
+    auto load_block_row = [&](int i, int slot) {
+#pragma unroll
+        for (int q = 0; q < L; ++q)
+            dma16(rc_words, chunk_off(i, q), 0u,
+                  region_addr + (uint32_t)(slot * kSlotBytes + q * 1024));
+    };
+    // byte offset within a slot of this lane's accumulator element of row 4 g + r, block
+    // column j (accumulator register r of block (i, j) is row 16 i + 4 (lane / 16) + r,
+    // column 16 j + lane % 16)
+    const int g = lane / 16, u = lane % 16;
+    auto c_at = [&](int j, int r) -> int {
+        const int colb = (16 * j + u) * OB;                 // byte column in the row
+        return (4 * g + r) * RB + ((((colb >> 4) ^ swz(4 * g + r))) << 4) + (colb & 15);
+    };
+
+    if constexpr (kReadC)
+        static_for<S>([&](auto t_c) { load_block_row(decltype(t_c)::value, decltype(t_c)::value); });
+    static_for<FM>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        lds_char *slot = region + (i % S) * kSlotBytes;
+        CT cv[FN][4];
+        if constexpr (kReadC) {
+            constexpr int after = c_ops_after(i, S, FM, L, L);
+            wait_vmem<(after < 63 ? after : 63)>();      // block row i's C is in its slot
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) cv[j][r] = Out<OUT>::lds_load(slot + c_at(j, r));
+        } else if constexpr (i >= S) {
+            wait_lds<0>();       // the slot's previous block row has been read back
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (kInt) {
+                    uint32_t v = (uint32_t)p.alpha_i * (uint32_t)acc[i][j][r];
+                    if constexpr (kReadC) v += (uint32_t)p.beta_i * (uint32_t)cv[j][r];
+                    Out<OUT>::lds_store(slot + c_at(j, r), (int)v);
+                } else if constexpr (kReadC) {
+                    // one rounding of beta * c, then alpha * acc + (beta * c) fused
+                    Out<OUT>::lds_store(slot + c_at(j, r),
+                                        __builtin_fmaf(p.alpha_f, acc[i][j][r], p.beta_f * cv[j][r]));
+                } else {
+                    Out<OUT>::lds_store(slot + c_at(j, r), p.alpha_f * acc[i][j][r]);
+                }
+            }
+        // the wave's LDS operations run in order: the reads below see the writes above
+#pragma unroll
+        for (int q = 0; q < L; ++q) {
+            const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(slot + q * 1024 + 16 * lane);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rd, (int)chunk_off(i, q), 0, 0);
+        }
+        if constexpr (kReadC && i + S < FM) {
+            wait_lds<0>();                                  // the slot's values are in registers
+            load_block_row(i + S, i % S);
+        }
+    });
+}
+
+// ---------------------------------------------------------------------------------------
+// One BM x BN tile of D (tile row tm, tile column tn) by one workgroup; smem holds at least
+// kBuffers (BM + BN) 128 bytes of LDS.
+// ---------------------------------------------------------------------------------------
+template <int IN, int OUT, bool TA, bool TB, int BM, int BN, int NW>
+__device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_char *smem) {
     constexpr bool kF8 = is_fp8(IN);
+    static_assert(NW == 4 || (NW == 8 && !kF8), "4 waves, or 8 for 2-byte and INT8 inputs");
     constexpr int EB = (IN == IN_I8 || kF8) ? 1 : 2;
     constexpr int NSA = BM / 32, NSB = BN / 32;
-    constexpr int FM = BM / 32, FN = BN / 32;   // 16-wide MFMA blocks per wave (2 x 2 wave grid)
+    // 16-wide MFMA blocks per wave: a 2 x (NW / 2) wave grid
+    constexpr int FM = BM / 32, FN = BN / (8 * NW);
     constexpr int kStageK = kStageKBytes / EB;
-    using OpA = Operand<EB, !TA, NSA>;
-    using OpB = Operand<EB, TB, NSB>;
+    using OpA = Operand<EB, !TA, NSA, NW / 4>;
+    using OpB = Operand<EB, TB, NSB, NW / 4>;
     using acc_t = typename MmaAcc<IN>::type;
     constexpr int A_BYTES = OpA::kStageBytes, B_BYTES = OpB::kStageBytes;
     constexpr int kLoadsPerStage = OpA::kSlots + OpB::kSlots;   // per wave
@@ -704,25 +830,23 @@ void gemm_kernel(Params p) {
     // LDS: [A stage 0 | A stage 1 | B stage 0 | B stage 1].  Stage parity is a compile-time
     // constant in the unrolled loop below, so every fragment read is one base register plus
     // an immediate offset.
-    __shared__ __attribute__((aligned(16))) char smem_raw[kBuffers * (A_BYTES + B_BYTES)];
-    lds_char *smem = (lds_char *)smem_raw;
     auto stage_a = [&](int parity) { return smem + parity * A_BYTES; };
     auto stage_b = [&](int parity) { return smem + kBuffers * A_BYTES + parity * B_BYTES; };
 
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64;
-    const int wm = wave >> 1, wn = wave & 1;
+    // With 8 waves, waves w and w + 4 (wm = 0 and 1) share a SIMD and a column of B blocks.
+    const int wm = wave / (NW / 2), wn = wave % (NW / 2);
+    const int vq = wave & 3, hi = wave >> 2;    // the quarter and position group it loads
 
-    int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int m_left = p.m - m0, n_left = p.n - n0;
     const bool full_mn = (m_left >= BM) && (n_left >= BN);
 
     OpA opa;
     OpB opb;
-    opa.init(wave, lane, p.lda, m_left, 0u);
-    opb.init(wave, lane, p.ldb, n_left, (uint32_t)(kBuffers * A_BYTES));
+    opa.init(vq, hi, lane, p.lda, m_left, 0u);
+    opb.init(vq, hi, lane, p.ldb, n_left, (uint32_t)(kBuffers * A_BYTES));
 
     const int nk = (p.k + kStageK - 1) / kStageK;
     const int k_tail = p.k % kStageK;
@@ -754,14 +878,15 @@ void gemm_kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = acc_t{};
 
-    const uint32_t lds_w = (uint32_t)(uintptr_t)smem + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
+    const uint32_t lds_w = (uint32_t)(uintptr_t)smem +
+                           (uint32_t)__builtin_amdgcn_readfirstlane(hi * 4096 + vq * 1024);
     // K ends inside the last stage: its K-contiguous chunks past K are zeroed once they have
     // landed (wave-uniform test).
     auto fix_stage = [&](int s, int parity) {
         if (k_tail != 0 && s == nk - 1) {
             wait_vmem<0>();  // this lane's chunks have landed
-            opa.fix_k_tail(stage_a(parity), k_tail);
-            opb.fix_k_tail(stage_b(parity), k_tail);
+            opa.fix_k_tail(stage_a(parity), k_tail, vq, hi, lane);
+            opb.fix_k_tail(stage_b(parity), k_tail, vq, hi, lane);
         }
     };
 
@@ -1006,36 +1131,50 @@ void gemm_kernel(Params p) {
     // addresses are computed after the loop rather than held in registers across it.
     int lane_e = lane;
     asm volatile("" : "+v"(lane_e));
-    if (p.read_c) {
-        // every wave's loads and fragment reads are complete: the LDS is free for C
+    constexpr int kRegion = kBuffers * (A_BYTES + B_BYTES) / NW;  // LDS bytes per wave
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    lds_char *region = smem + w * kRegion;
+    const uint32_t region_addr = (uint32_t)(uintptr_t)smem + (uint32_t)(w * kRegion);
+    if (full_mn) {
+        // every wave's loads and fragment reads are complete: the LDS is free
         __syncthreads();
-        constexpr int kRegion = kBuffers * (A_BYTES + B_BYTES) / 4;   // LDS bytes per wave
-        const int w = __builtin_amdgcn_readfirstlane(wave);
-        const lds_char *region = smem + w * kRegion;
-        const uint32_t region_addr = (uint32_t)(uintptr_t)smem + (uint32_t)(w * kRegion);
-        if (full_mn)
-            store_tile_c_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, true>(
-                p, acc, m0, n0, wm, wn, lane_e, m_left, n_left, region, region_addr);
+        if (p.read_c)
+            store_full_tile_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, NW, true>(
+                p, acc, m0, n0, wm, wn, lane_e, region, region_addr);
         else
-            store_tile_c_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, false>(
-                p, acc, m0, n0, wm, wn, lane_e, m_left, n_left, region, region_addr);
-    } else if (full_mn) {
-        store_tile<IN == IN_I8, OUT, FM, FN, BM, BN, true>(p, acc, m0, n0, wm, wn, lane_e, m_left,
-                                                           n_left);
+            store_full_tile_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, NW, false>(
+                p, acc, m0, n0, wm, wn, lane_e, region, region_addr);
+    } else if (p.read_c) {
+        __syncthreads();
+        store_tile_c_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, false, NW>(
+            p, acc, m0, n0, wm, wn, lane_e, m_left, n_left, region, region_addr);
     } else {
-        store_tile<IN == IN_I8, OUT, FM, FN, BM, BN, false>(p, acc, m0, n0, wm, wn, lane_e, m_left,
-                                                            n_left);
+        store_tile<IN == IN_I8, OUT, FM, FN, BM, BN, false, NW>(p, acc, m0, n0, wm, wn, lane_e,
+                                                                m_left, n_left);
     }
+}
+
+// ---------------------------------------------------------------------------------------
+// The kernel: one tile per workgroup.
+// ---------------------------------------------------------------------------------------
+template <int IN, int OUT, bool TA, bool TB, int BM, int BN, int NW = 4>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void gemm_kernel(Params p) {
+    __shared__ __attribute__((aligned(16))) char smem_raw[kBuffers * (BM + BN) * kStageKBytes];
+    int tm, tn;
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    gemm_tile<IN, OUT, TA, TB, BM, BN, NW>(p, tm, tn, (lds_char *)smem_raw);
 }
 
 // Host-side launcher of one instance.  hipLaunchKernel returns this launch's own status (an
 // error the caller left pending on the thread is neither reported nor cleared).
-template <int IN, int OUT, bool TA, bool TB, int BM, int BN>
+template <int IN, int OUT, bool TA, bool TB, int BM, int BN, int NW = 4>
 hipError_t launch(const Params &p, hipStream_t stream) {
     const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
     void *args[] = {const_cast<Params *>(&p)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<IN, OUT, TA, TB, BM, BN>),
-                           dim3(grid), dim3(kThreads), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<IN, OUT, TA, TB, BM, BN, NW>),
+                           dim3(grid), dim3(NW * 64), args, 0, stream);
 }
 
 // Entry points of the per-input-type translation units.
