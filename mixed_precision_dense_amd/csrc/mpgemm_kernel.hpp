@@ -5,8 +5,9 @@
 // whose accumulators stay in the accumulation registers for the whole K loop.  K is walked in
 // stages of 128 bytes per row (64 FP16/BF16 or 128 INT8 elements, two MFMA k steps of 64
 // bytes).  Stages are copied from global memory straight into LDS by direct-to-LDS buffer
-// loads (whole 128-byte lines per row) into one of two buffers while the waves multiply out
-// of the other.
+// loads (whole 128-byte lines per row) into free buffers -- two for A, three for B -- while
+// the waves multiply out of another; each of a stage's two k steps queues half of the loads
+// of the stage two ahead (B's in the first, A's in the second).
 //
 // The structure follows the pages' description of a tensor-core GEMM, re-planned for CDNA4:
 //   * the product is a sum of rank-k slabs, each slab an outer product of a column panel of
@@ -14,7 +15,7 @@
 //   * slabs are staged in on-chip shared memory in a block tile, each wave multiplying
 //     fragments of it ("The CUDA Handbook" section 17.5, Listing 17-5 and the paragraph after
 //     it, which also observes that the wait for the next slab's global load becomes the
-//     bottleneck -- hence the double buffer filled while the other is multiplied here);
+//     bottleneck -- hence the stage buffers filled while another is multiplied here);
 //   * the accumulator starts at zero, the K loop accumulates in place, and the epilogue scales
 //     the product by alpha and adds beta * C element by element before storing
 //     ("Programming Tensor Cores in CUDA 9", sections "Inner loop" and "Finishing");
@@ -32,8 +33,8 @@
 // lane l holds row (A) or column (B) l % 16 and the 16-byte k chunk l / 16 of the 64-byte k
 // step.  Accumulator register r of lane l holds row 4 * (l / 16) + r, column l % 16.
 //
-// LDS layout: [A stage 0 | A stage 1 | B stage 0 | B stage 1].  Each operand's stage is a row
-// of 4 KB sub-tiles of 32 rows (K-contiguous) or a row of 128-byte column groups
+// LDS layout: [A stage 0 | A stage 1 | B stage 0 | B stage 1 | B stage 2] (FP8: two B
+// stages).  Each operand's stage is a row of 4 KB sub-tiles of 32 rows (K-contiguous) or a row of 128-byte column groups
 // (MN-contiguous), so that fragment addresses differ only by immediate offsets.
 //   * K-contiguous operand (A with transa = N, B with transb = T): sub-tile = 32 rows x 128 B,
 //     16-byte chunk c of row r at chunk position c ^ kc_swz(r), which keeps a fragment read
@@ -102,7 +103,10 @@ __device__ __forceinline__ void static_for(F &&f) {
 constexpr int kStageKBytes = 128;   // bytes of k per row per stage (two MFMA k steps)
 constexpr int kStepKBytes = 64;     // bytes of k per row per MFMA k step
 constexpr int kSubTileBytes = 4096; // 32 rows x 128 B, or the transposed equivalent
-constexpr int kBuffers = 2;         // LDS double buffer
+constexpr int kBuffers = 2;         // LDS buffers of A's stages (and of B's for FP8)
+// LDS buffers of B's stages: three for 2-byte and INT8 inputs, so that a stage's B loads can be
+// queued a k step before its A loads (see gemm_tile)
+constexpr int b_buffers(int in) { return is_fp8(in) ? 2 : 3; }
 constexpr int kGroupM = 4;          // tile-row grouping for L2 reuse
 constexpr uint32_t kOobOffset = 0x80000000u;  // a buffer offset past every resource's range
 constexpr int kNumRecords = 0x7FFFFFFF;
@@ -808,9 +812,16 @@ __device__ __forceinline__ void store_full_tile_staged(const Params &p, AccT (&a
     });
 }
 
+// LDS bytes of one workgroup: the A and B stage buffers of 128 bytes per row (160 KB, all of
+// a CU's LDS, at 256 x 256 with three B buffers)
+template <int IN, int BM, int BN>
+constexpr int tile_lds_bytes() {
+    return (kBuffers * BM + b_buffers(IN) * BN) * kStageKBytes;
+}
+
 // ---------------------------------------------------------------------------------------
 // One BM x BN tile of D (tile row tm, tile column tn) by one workgroup; smem holds at least
-// kBuffers (BM + BN) 128 bytes of LDS.
+// tile_lds_bytes() of LDS.
 // ---------------------------------------------------------------------------------------
 template <int IN, int OUT, bool TA, bool TB, int BM, int BN, int NW>
 __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_char *smem) {
@@ -881,37 +892,37 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
     const uint32_t lds_w = (uint32_t)(uintptr_t)smem +
                            (uint32_t)__builtin_amdgcn_readfirstlane(hi * 4096 + vq * 1024);
     // K ends inside the last stage: its K-contiguous chunks past K are zeroed once they have
-    // landed (wave-uniform test).
-    auto fix_stage = [&](int s, int parity) {
+    // landed (wave-uniform test).  pa: the stage's A buffer; b_off: its B buffer's offset
+    // from the first B buffer.
+    auto fix_stage = [&](int s, int pa, uint32_t b_off) {
         if (k_tail != 0 && s == nk - 1) {
             wait_vmem<0>();  // this lane's chunks have landed
-            opa.fix_k_tail(stage_a(parity), k_tail, vq, hi, lane);
-            opb.fix_k_tail(stage_b(parity), k_tail, vq, hi, lane);
+            opa.fix_k_tail(stage_a(pa), k_tail, vq, hi, lane);
+            opb.fix_k_tail(stage_b(0) + b_off, k_tail, vq, hi, lane);
         }
     };
 
     if constexpr (!kF8) {
         // Fragment registers: two sets, one per k step of a stage.
         u32x4 fa[2][FM], fb[2][FN];
-        // read unit u (< FM + FN): fragment u of A, or fragment u - FM of B
-        auto read_unit = [&](int set, int parity, int ks, int u) {
+        // read unit u (< FM + FN) of k step ks: fragment u of A from A buffer pa, or fragment
+        // u - FM of B from the B buffer at b_off
+        auto read_unit = [&](int set, int pa, uint32_t b_off, int ks, int u) {
             if (u < FM)
-                fa[set][u] = opa.frag(smem + parity * A_BYTES, wm * FM + u, ks);
+                fa[set][u] = opa.frag(smem + pa * A_BYTES, wm * FM + u, ks);
             else
-                fb[set][u - FM] = opb.frag(smem + parity * B_BYTES, wn * FN + (u - FM), ks);
+                fb[set][u - FM] = opb.frag(smem + b_off, wn * FN + (u - FM), ks);
         };
-        // Loads of one stage: A slots first, then B slots; rs_a / rs_b address the stage.
+        // Load slot l of a stage's A (into A buffer pa) or B (into the B buffer at b_off);
+        // rs_a / rs_b address the stage.
         i32x4 rs_a, rs_b;
-        auto load_slot = [&](int parity, int l) {
-            if (l < OpA::kSlots)
-                opa.load(rs_a, lds_w + (uint32_t)(parity * A_BYTES), l);
-            else
-                opb.load(rs_b, lds_w + (uint32_t)(kBuffers * A_BYTES + parity * B_BYTES), l - OpA::kSlots);
+        auto load_a = [&](int pa, int l) { opa.load(rs_a, lds_w + (uint32_t)(pa * A_BYTES), l); };
+        auto load_b = [&](uint32_t b_off, int l) {
+            opb.load(rs_b, lds_w + (uint32_t)(kBuffers * A_BYTES) + b_off, l);
         };
         // Prepare the resources of stage s (the cursors then move to stage s + 1).
         auto next_rsrc_a = [&](int s) { rs_a = ca.rsrc(s, nk); ca.advance(); keep_here(rs_a); keep_here(ca.base); };
         auto next_rsrc_b = [&](int s) { rs_b = cb.rsrc(s, nk); cb.advance(); keep_here(rs_b); keep_here(cb.base); };
-        auto no_hook = [&](auto) {};
         // In the loop the same resources are prepared in eight pieces of one or two scalar
         // instructions (for A, then B: the record count in two selects, the words, the
         // advance), each pinned in its own gap between MFMAs.
@@ -927,14 +938,14 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
             if constexpr (p % 4 == 3) { c.advance(); keep_here(c.base); }
         };
 
-        // One k step: the FM x FN MFMAs of fragment set `set`, each in its own fenced group with at
-        // most two other instructions -- a wave issues one instruction per four cycles, so more
-        // would hold back the next 16-cycle MFMA.  The fragments of the next k step (into the
-        // other set) are read at the even MFMAs of the first half; the `nl` load slots of the
-        // stage being refilled go to every (kMf / nl)-th MFMA from the second one on.
+        // One k step: the FM x FN MFMAs of fragment set `set`, each in its own fenced group with
+        // at most two other instructions -- a wave issues one instruction per four cycles, so
+        // more would hold back the next 16-cycle MFMA.  The fragments of the next k step (into
+        // the other set) are read at the even MFMAs of the first half; `extra` places the
+        // step's resource pieces and loads.
         constexpr int kMf = FM * FN, kUnits = FM + FN;
-        auto k_step = [&](auto set_c, int rd_parity, int rd_ks, int ld_parity, auto nl_c, auto &&hook) {
-            constexpr int set = decltype(set_c)::value, nl = decltype(nl_c)::value;
+        auto k_step = [&](auto set_c, int rd_pa, uint32_t rd_b, int rd_ks, auto &&extra) {
+            constexpr int set = decltype(set_c)::value;
             // The fragments of this k step were read during the first half of the previous one:
             // one wait for all of them instead of a wait before each MFMA that uses a new one.
             wait_lds<0>();
@@ -942,64 +953,102 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
                 constexpr int idx = decltype(idx_c)::value;
                 constexpr int i = idx / FN, j = idx % FN;
                 Mma<IN>::run(fa[set][i], fb[set][j], acc[i][j]);
-                hook(idx_c);
+                extra(idx_c);
                 static_for<kUnits>([&](auto u_c) {
                     constexpr int u = decltype(u_c)::value;
                     constexpr int at = 2 * kUnits <= kMf ? 2 * u : (u * kMf) / kUnits;
-                    if constexpr (at == idx) read_unit(set ^ 1, rd_parity, rd_ks, u);
-                });
-                static_for<nl>([&](auto l_c) {
-                    constexpr int l = decltype(l_c)::value;
-                    constexpr int at = ((l * kMf) / (nl > 0 ? nl : 1) + 1) % kMf;
-                    if constexpr (at == idx) load_slot(ld_parity, l);
+                    if constexpr (at == idx) read_unit(set ^ 1, rd_pa, rd_b, rd_ks, u);
                 });
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;
-        using CL = std::integral_constant<int, kLoadsPerStage>;
 
-        // Stage s multiplies out of LDS buffers s % 2 in two k steps.  During k step 0 the waves
-        // read the fragments of k step 1.  Then each wave waits (vmcnt) for its loads of stage
-        // s + 1, and one barrier publishes stage s + 1 and certifies that every wave has read its
-        // last fragments of stage s.  During k step 1 the waves read the first fragments of stage
-        // s + 1 and queue the loads of stage s + 2 into the buffers just freed, so every load has
-        // at least one k step to land before the barrier that waits for it.
-        // The resources of stage s + 2 are prepared in odd MFMA groups of k step 0, a few scalar
-        // instructions at a time.
+        // A stage's loads are split between its two k steps so that each carries half of them:
+        // measured per k step, one that issues a whole stage's loads (16 per wave at 256 x 256)
+        // runs at 64-85 % of the MFMA issue rate, one with half of them at 93 %, against 97 %
+        // for one with none.  A is double-buffered and B triple-buffered (LDS:
+        // [A 0 | A 1 | B 0 | B 1 | B 2]):
+        //   k step 0 of stage s multiplies its first k half out of registers, reads the
+        //     fragments of the second, and queues the B loads of stage s + 2 into the B buffer
+        //     stage s - 1 has left (free since the barrier of stage s - 1);
+        //   each wave then waits for its loads of stage s + 1 (the B loads just queued may stay
+        //     in flight), and one barrier publishes stage s + 1 and certifies that every wave
+        //     has read its last fragments of stage s;
+        //   k step 1 multiplies the second k half, reads the first fragments of stage s + 1, and
+        //     queues the A loads of stage s + 2 into the A buffer stage s has just left.
+        // Every load has at least one k step to land before the barrier that waits for it; B's
+        // (the operand whose loads land last on row-major NN products) have a stage and a half.
+        // The resources of stage s + 2 are prepared in k step 0, a few scalar instructions at a
+        // time: B's pieces first, at the first odd MFMAs, then B's loads at later odd MFMAs, and
+        // A's pieces at even MFMAs past the fragment reads.  The B buffer offsets rotate by one
+        // buffer per stage: b_cur (stage s), b_next (s + 1), b_load (s + 2).
+        constexpr int kLoadsB = OpB::kSlots, kLoadsA = OpA::kSlots;
+        uint32_t b_cur = 0, b_next = B_BYTES, b_load = 2 * B_BYTES;
         auto stage_iter = [&](int s, auto par_c) {
             constexpr int P = decltype(par_c)::value;
-            k_step(C0{}, P, 1, 0, C0{}, [&](auto idx_c) {
+            k_step(C0{}, P, b_cur, 1, [&](auto idx_c) {
                 constexpr int idx = decltype(idx_c)::value;
-                static_for<8>([&](auto p_c) {
-                    // the odd MFMAs of the second half, which have no fragment reads beside them
-                    constexpr int p = decltype(p_c)::value;
-                    constexpr int at = kMf >= 16 ? (kMf / 2 + 1 + 2 * p) % kMf : 1 % kMf;
-                    if constexpr (at == idx) rsrc_piece(p_c, s + 2);
-                });
+                if constexpr (kMf >= 64) {
+                    static_for<4>([&](auto q_c) {
+                        constexpr int q = decltype(q_c)::value;
+                        if constexpr (idx == 2 * q + 1)
+                            rsrc_piece(std::integral_constant<int, 4 + q>{}, s + 2);
+                        if constexpr (idx == 2 * kUnits + 2 * q)
+                            rsrc_piece(std::integral_constant<int, q>{}, s + 2);
+                    });
+                    static_for<kLoadsB>([&](auto l_c) {
+                        constexpr int l = decltype(l_c)::value;
+                        constexpr int span = (kMf - 10) / 2;
+                        constexpr int at = 9 + 2 * ((l * span) / (kLoadsB > 1 ? kLoadsB - 1 : 1));
+                        if constexpr (at == idx) load_b(b_load, l);
+                    });
+                } else {
+                    // short k steps (smaller tiles): every piece beside the first MFMA
+                    if constexpr (idx == 0) {
+                        static_for<4>([&](auto q_c) { rsrc_piece(std::integral_constant<int, 4 + decltype(q_c)::value>{}, s + 2); });
+                        static_for<4>([&](auto q_c) { rsrc_piece(q_c, s + 2); });
+                    }
+                    static_for<kLoadsB>([&](auto l_c) {
+                        constexpr int l = decltype(l_c)::value;
+                        if constexpr (((l * kMf) / kLoadsB + 1) % kMf == idx) load_b(b_load, l);
+                    });
+                }
             });
-            wait_vmem<0>();  // this wave's loads of stage s + 1 have landed
-            fix_stage(s + 1, P ^ 1);
+            wait_vmem<kLoadsB>();  // this wave's loads of stage s + 1 have landed
+            fix_stage(s + 1, P ^ 1, b_next);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
-            k_step(C1{}, P ^ 1, 0, P, CL{}, no_hook);
+            k_step(C1{}, P ^ 1, b_next, 0, [&](auto idx_c) {
+                constexpr int idx = decltype(idx_c)::value;
+                static_for<kLoadsA>([&](auto l_c) {
+                    constexpr int l = decltype(l_c)::value;
+                    if constexpr (((l * kMf) / kLoadsA + 1) % kMf == idx) load_a(P, l);
+                });
+            });
+            const uint32_t b_free = b_cur;
+            b_cur = b_next;
+            b_next = b_load;
+            b_load = b_free;
         };
 
         // Prologue: stages 0 and 1 are queued; wait for stage 0.
         next_rsrc_a(0);
         next_rsrc_b(0);
-        static_for<kLoadsPerStage>([&](auto l_c) { load_slot(0, decltype(l_c)::value); });
+        static_for<kLoadsA>([&](auto l_c) { load_a(0, decltype(l_c)::value); });
+        static_for<kLoadsB>([&](auto l_c) { load_b(0, decltype(l_c)::value); });
         next_rsrc_a(1);
         next_rsrc_b(1);
-        static_for<kLoadsPerStage>([&](auto l_c) { load_slot(1, decltype(l_c)::value); });
+        static_for<kLoadsA>([&](auto l_c) { load_a(1, decltype(l_c)::value); });
+        static_for<kLoadsB>([&](auto l_c) { load_b(B_BYTES, decltype(l_c)::value); });
         wait_vmem<kLoadsPerStage>();
-        fix_stage(0, 0);
+        fix_stage(0, 0, 0);
         __syncthreads();
     #pragma unroll
-        for (int u = 0; u < kUnits; ++u) read_unit(0, 0, 0, u);
+        for (int u = 0; u < kUnits; ++u) read_unit(0, 0, 0, 0, u);
 
-        // Stages are taken in pairs (buffer parity 0, then 1).  For an odd number of stages the
+        // Stages are taken in pairs (A buffer parity 0, then 1).  For an odd number of stages the
         // last pair's second stage lies past K: its loads read zero records, so it multiplies zeros
         // into the accumulators, which leaves them unchanged.
         for (int s = 0; s < nk; s += 2) {
@@ -1091,7 +1140,7 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
             constexpr int P = decltype(par_c)::value;
             half0(s, par_c);
             wait_vmem<0>();  // this wave's loads of stage s + 1 have landed
-            fix_stage(s + 1, P ^ 1);
+            fix_stage(s + 1, P ^ 1, (uint32_t)((P ^ 1) * B_BYTES));
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
             half1(par_c);
@@ -1106,7 +1155,7 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
         next_rsrc_b(1);
         static_for<kLoadsPerStage>([&](auto l_c) { load_slot(1, decltype(l_c)::value); });
         wait_vmem<kLoadsPerStage>();
-        fix_stage(0, 0);
+        fix_stage(0, 0, 0u);
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < 2 * HM; ++r) read_a(0, r / 2, r % 2);
@@ -1161,7 +1210,7 @@ template <int IN, int OUT, bool TA, bool TB, int BM, int BN, int NW = 4>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) char smem_raw[kBuffers * (BM + BN) * kStageKBytes];
+    __shared__ __attribute__((aligned(16))) char smem_raw[tile_lds_bytes<IN, BM, BN>()];
     int tm, tn;
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
     gemm_tile<IN, OUT, TA, TB, BM, BN, NW>(p, tm, tn, (lds_char *)smem_raw);
