@@ -33,9 +33,9 @@
 // lane l holds row (A) or column (B) l % 16 and the 16-byte k chunk l / 16 of the 64-byte k
 // step.  Accumulator register r of lane l holds row 4 * (l / 16) + r, column l % 16.
 //
-// LDS layout: [A stage 0 | A stage 1 | B stage 0 | B stage 1 | B stage 2] (FP8: two B
-// stages).  Each operand's stage is a row of 4 KB sub-tiles of 32 rows (K-contiguous) or a row of 128-byte column groups
-// (MN-contiguous), so that fragment addresses differ only by immediate offsets.
+// LDS layout: [A stage 0 | A stage 1 | B stage 0 | B stage 1 | B stage 2].  Each operand's
+// stage is a row of 4 KB sub-tiles of 32 rows (K-contiguous) or a row of 128-byte column
+// groups (MN-contiguous), so that fragment addresses differ only by immediate offsets.
 //   * K-contiguous operand (A with transa = N, B with transb = T): sub-tile = 32 rows x 128 B,
 //     16-byte chunk c of row r at chunk position c ^ kc_swz(r), which keeps a fragment read
 //     free of bank conflicts (see kc_swz).
@@ -103,10 +103,10 @@ __device__ __forceinline__ void static_for(F &&f) {
 constexpr int kStageKBytes = 128;   // bytes of k per row per stage (two MFMA k steps)
 constexpr int kStepKBytes = 64;     // bytes of k per row per MFMA k step
 constexpr int kSubTileBytes = 4096; // 32 rows x 128 B, or the transposed equivalent
-constexpr int kBuffers = 2;         // LDS buffers of A's stages (and of B's for FP8)
-// LDS buffers of B's stages: three for 2-byte and INT8 inputs, so that a stage's B loads can be
-// queued a k step before its A loads (see gemm_tile)
-constexpr int b_buffers(int in) { return is_fp8(in) ? 2 : 3; }
+constexpr int kBuffers = 2;         // LDS buffers of A's stages
+// LDS buffers of B's stages: three, so that a stage's B loads can be queued a k step (FP8: a
+// half stage) before its A loads (see gemm_tile)
+constexpr int b_buffers(int) { return 3; }
 constexpr int kGroupM = 4;          // tile-row grouping for L2 reuse
 constexpr uint32_t kOobOffset = 0x80000000u;  // a buffer offset past every resource's range
 constexpr int kNumRecords = 0x7FFFFFFF;
@@ -1073,24 +1073,28 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
         auto read_a = [&](int parity, int blk, int ks) {
             set_half(fa8[blk], ks, opa.frag(smem + parity * A_BYTES, wm * FM + blk, ks));
         };
-        auto read_b = [&](int parity, int blk, int ks) {
-            set_half(fb8[blk], ks, opb.frag(smem + parity * B_BYTES, wn * FN + blk, ks));
+        // B from the B buffer at b_off (three buffers, rotating as in the 2-byte path)
+        auto read_b = [&](uint32_t b_off, int blk, int ks) {
+            set_half(fb8[blk], ks, opb.frag(smem + b_off, wn * FN + blk, ks));
         };
         i32x4 rs_a, rs_b;
-        auto load_slot = [&](int parity, int l) {
-            if (l < OpA::kSlots)
-                opa.load(rs_a, lds_w + (uint32_t)(parity * A_BYTES), l);
-            else
-                opb.load(rs_b, lds_w + (uint32_t)(kBuffers * A_BYTES + parity * B_BYTES), l - OpA::kSlots);
+        auto load_a = [&](int pa, int l) { opa.load(rs_a, lds_w + (uint32_t)(pa * A_BYTES), l); };
+        auto load_b = [&](uint32_t b_off, int l) {
+            opb.load(rs_b, lds_w + (uint32_t)(kBuffers * A_BYTES) + b_off, l);
         };
+        constexpr int kLoadsB = OpB::kSlots, kLoadsA = OpA::kSlots;
+        uint32_t b_cur = 0, b_next = B_BYTES, b_load = 2 * B_BYTES;
         auto next_rsrc_a = [&](int s) { rs_a = ca.rsrc(s, nk); ca.advance(); keep_here(rs_a); keep_here(ca.base); };
         auto next_rsrc_b = [&](int s) { rs_b = cb.rsrc(s, nk); cb.advance(); keep_here(rs_b); keep_here(cb.base); };
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;
 
-        // Half 0 of stage s (buffers P): the last B block's two reads (issued after the last
+        // Half 0 of stage s (A buffer P): the last B block's two reads (issued after the last
         // MFMA of the previous half 1) may still be in flight; they are waited for just before
-        // that block's first MFMA, past the A reads this half has issued by then.
+        // that block's first MFMA, past the A reads this half has issued by then.  B's loads of
+        // stage s + 2 go to the B buffer stage s - 1 left (its last reads, in half 1 of stage
+        // s - 2, were certified by the barrier of stage s - 1); A's follow in half 1, so each half
+        // carries half of a stage's loads.
         auto half0 = [&](int s, auto par_c) {
             constexpr int P = decltype(par_c)::value;
             wait_lds<2>();
@@ -1105,11 +1109,16 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
                     constexpr int r = decltype(r_c)::value;
                     if constexpr (2 * r == t) read_a(P, HM + r / 2, r % 2);
                 });
+                static_for<kLoadsB>([&](auto l_c) {    // past the B resource (MFMA 3)
+                    constexpr int l = decltype(l_c)::value;
+                    constexpr int at = kHalf > 4 ? 4 + (l * (kHalf - 4)) / kLoadsB : (3 + l) % kHalf;
+                    if constexpr (at == t) load_b(b_load, l);
+                });
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
-        // Half 1 of stage s: the next stage (buffers P ^ 1) is in LDS; the loads of stage s + 2
-        // go to buffers P, which every wave has finished reading.
+        // Half 1 of stage s: the next stage (A buffer P ^ 1, B buffer b_next) is in LDS; A's
+        // loads of stage s + 2 go to A buffer P, which every wave has finished reading.
         auto half1 = [&](auto par_c) {
             constexpr int P = decltype(par_c)::value;
             wait_lds<0>();
@@ -1124,14 +1133,14 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
                 static_for<FN>([&](auto jj_c) {        // next stage: B block jj after its last use
                     constexpr int jj = decltype(jj_c)::value;
                     if constexpr (t == (jj + 1) * HM - 1) {
-                        read_b(P ^ 1, jj, 0);
-                        read_b(P ^ 1, jj, 1);
+                        read_b(b_next, jj, 0);
+                        read_b(b_next, jj, 1);
                     }
                 });
-                static_for<kLoadsPerStage>([&](auto l_c) {
+                static_for<kLoadsA>([&](auto l_c) {
                     constexpr int l = decltype(l_c)::value;
-                    constexpr int at = ((l * kHalf) / kLoadsPerStage + 1) % kHalf;
-                    if constexpr (at == t) load_slot(P, l);
+                    constexpr int at = ((l * kHalf) / kLoadsA + 1) % kHalf;
+                    if constexpr (at == t) load_a(P, l);
                 });
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -1139,21 +1148,27 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
         auto stage8 = [&](int s, auto par_c) {
             constexpr int P = decltype(par_c)::value;
             half0(s, par_c);
-            wait_vmem<0>();  // this wave's loads of stage s + 1 have landed
-            fix_stage(s + 1, P ^ 1, (uint32_t)((P ^ 1) * B_BYTES));
+            wait_vmem<kLoadsB>();  // this wave's loads of stage s + 1 have landed
+            fix_stage(s + 1, P ^ 1, b_next);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
             half1(par_c);
+            const uint32_t b_free = b_cur;
+            b_cur = b_next;
+            b_next = b_load;
+            b_load = b_free;
         };
 
         // Prologue: stages 0 and 1 queued, stage 0 waited for; then the fragments half 0 of
         // stage 0 needs first (A blocks 0 .. HM-1, every B block; the last B block last).
         next_rsrc_a(0);
         next_rsrc_b(0);
-        static_for<kLoadsPerStage>([&](auto l_c) { load_slot(0, decltype(l_c)::value); });
+        static_for<kLoadsA>([&](auto l_c) { load_a(0, decltype(l_c)::value); });
+        static_for<kLoadsB>([&](auto l_c) { load_b(0, decltype(l_c)::value); });
         next_rsrc_a(1);
         next_rsrc_b(1);
-        static_for<kLoadsPerStage>([&](auto l_c) { load_slot(1, decltype(l_c)::value); });
+        static_for<kLoadsA>([&](auto l_c) { load_a(1, decltype(l_c)::value); });
+        static_for<kLoadsB>([&](auto l_c) { load_b(B_BYTES, decltype(l_c)::value); });
         wait_vmem<kLoadsPerStage>();
         fix_stage(0, 0, 0u);
         __syncthreads();
