@@ -532,11 +532,22 @@ def config_record(w, args) -> dict:
                   "worst_err_over_bound": round(rep.worst_ratio, 4)}
     pk = PEAK_TFLOPS[w.in_type]
     tf = w.flops / (ev["median_ms"] * 1e-3) / 1e12
-    return {"workload": w.name, "kernel_ms_median": round(ev["median_ms"], 5),
-            "TFLOPs": round(tf, 2), "pct_of_peak": round(100 * tf / pk, 2),
-            "counters": recorded_counters(w.name), "parity_full_output": parity,
-            "oracle_full_s": round(oracle_s, 2), "oracle_threads": oracle.num_threads(),
-            "oracle_GFLOPs": round(w.flops / oracle_s / 1e9, 2)}
+    rec = {"workload": w.name, "kernel_ms_median": round(ev["median_ms"], 5),
+           "TFLOPs": round(tf, 2), "pct_of_peak": round(100 * tf / pk, 2),
+           "counters": recorded_counters(w.name), "parity_full_output": parity,
+           "oracle_full_s": round(oracle_s, 4), "oracle_threads": oracle.num_threads(),
+           "oracle_GFLOPs": round(w.flops / oracle_s / 1e9, 2)}
+    if w.flops <= 2 * 256 ** 3:
+        # the smallest configuration is also timed on one host thread
+        threads = oracle.num_threads()
+        oracle.set_num_threads(1)
+        t0 = time.perf_counter()
+        oracle_call(w, inp, None)
+        t1 = time.perf_counter() - t0
+        oracle.set_num_threads(threads)
+        rec["oracle_1thread_s"] = round(t1, 4)
+        rec["oracle_1thread_GFLOPs"] = round(w.flops / t1 / 1e9, 2)
+    return rec
 
 
 def main() -> int:

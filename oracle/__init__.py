@@ -132,6 +132,8 @@ def _load() -> ctypes.CDLL:
                                                          i32, i32, i32, i32, i64, vp, vp, vp]
         lib.oracle_num_threads.restype = i32
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [i32]
         _lib = lib
     return _lib
 
@@ -139,6 +141,11 @@ def _load() -> ctypes.CDLL:
 def num_threads() -> int:
     """OpenMP threads the oracle's loops run on."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Run the oracle's loops on ``n`` OpenMP threads from now on (timing runs)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 # ----------------------------------------------------------------------------- formats

@@ -303,8 +303,9 @@ int oracle_round_array(const double *v, int64_t count, int otype, void *out)
     return -1;
 }
 
-/* Threads the OpenMP loops above run on. */
+/* Threads the OpenMP loops above run on, and a way to set them (n >= 1) for timing runs. */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_num_threads(int n) { if (n >= 1) omp_set_num_threads(n); }
 
 /* ======================================================================================
  * Block-FMA model of matrix-core FP16/BF16 accumulation (bit-exact reference).

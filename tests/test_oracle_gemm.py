@@ -333,3 +333,22 @@ def test_half_output_rounding_ties():
     for k, want in [(2049, 2048.0), (2051, 2052.0)]:
         r = run_fp(np.ones((1, k)), np.ones((k, 1)), "f16", False, False)
         assert oracle.decode(int(oracle.round_to(r.v, "f16")[0, 0]), "f16") == want
+
+
+def test_thread_count_does_not_change_results():
+    """The oracle's thread count (set to 1 for the single-thread timing of the smallest
+    configuration) changes only the schedule: each output's sum is computed by one thread in
+    the same order, so results are identical."""
+    rng = np.random.default_rng(11)
+    a = rng.integers(-3, 4, size=(70, 90)).astype(np.float64) * 0.37
+    b = rng.integers(-3, 4, size=(90, 50)).astype(np.float64) * 1.3
+    threads = oracle.num_threads()
+    try:
+        oracle.set_num_threads(1)
+        assert oracle.num_threads() == 1
+        r1 = run_fp(a, b, "f16", False, False)
+    finally:
+        oracle.set_num_threads(threads)
+    assert oracle.num_threads() == threads
+    rn = run_fp(a, b, "f16", False, False)
+    assert np.array_equal(r1.v, rn.v) and np.array_equal(r1.S, rn.S)
