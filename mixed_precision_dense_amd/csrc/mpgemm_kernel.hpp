@@ -313,6 +313,38 @@ struct Operand {
         }
     }
 
+    // Fragment reads as a base register plus an immediate: kReadBases bases per stage buffer
+    // and wave (K-contiguous: one per k step; MN-contiguous: one per block position in a column
+    // group), each read_base(stage LDS address, i, the wave's first block), which for an
+    // MN-contiguous operand must be a multiple of kGroupBlocks.
+    static constexpr int kReadBases = KC ? 2 : kGroupBlocks;
+    __device__ __forceinline__ uint32_t read_base(uint32_t stage_addr, int i, int first_blk) const {
+        if constexpr (KC)
+            return stage_addr + r_off[i] + (uint32_t)(first_blk * 16 * kStageKBytes);
+        else
+            return stage_addr + r_off[i] + (uint32_t)((first_blk / kGroupBlocks) * kGroupBytes);
+    }
+    // Fragment of the wave's block j at k step ks from its base: base index ks (K-contiguous)
+    // or j mod kGroupBlocks (MN-contiguous).
+    __device__ __forceinline__ u32x4 frag_at(uint32_t base, int j, int ks) const {
+        typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+        if constexpr (KC) {
+            return *(const lds_u32x4 *)(lds_char *)(uintptr_t)(base + (uint32_t)(j * 16 * kStageKBytes));
+        } else if constexpr (EB == 2) {
+            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            const uint32_t a = base + (uint32_t)((j / kGroupBlocks) * kGroupBytes + ks * kStepK * 128);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lds_char *)(uintptr_t)a);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lds_char *)(uintptr_t)(a + 4 * 128));
+            return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+            typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+            const uint32_t a = base + (uint32_t)((j / kGroupBlocks) * kGroupBytes + ks * kStepK * 128);
+            const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(lds_char *)(uintptr_t)a);
+            const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(lds_char *)(uintptr_t)(a + 8 * 128));
+            return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
+        }
+    }
+
     // 16-byte MFMA operand of 16-wide block `blk` at k step `ks` (0 or 1) of a stage; `stage`
     // is the LDS start plus the stage's offset from this operand's first stage.
     __device__ __forceinline__ u32x4 frag(const lds_char *stage, int blk, int ks) const {
@@ -905,20 +937,42 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
     if constexpr (!kF8) {
         // Fragment registers: two sets, one per k step of a stage.
         u32x4 fa[2][FM], fb[2][FN];
-        // read unit u (< FM + FN) of k step ks: fragment u of A from A buffer pa, or fragment
-        // u - FM of B from the B buffer at b_off
-        auto read_unit = [&](int set, int pa, uint32_t b_off, int ks, int u) {
-            if (u < FM)
-                fa[set][u] = opa.frag(smem + pa * A_BYTES, wm * FM + u, ks);
-            else
-                fb[set][u - FM] = opb.frag(smem + b_off, wn * FN + (u - FM), ks);
+        constexpr int kMf = FM * FN, kUnits = FM + FN;
+        // B's buffer offset changes every stage (three buffers against A's two), so its fragment
+        // addresses are not immediates: at 128 x 128 per wave the kReadBases base registers of
+        // the next stage's B buffer are set once per stage (set_bases, pinned in MFMA groups
+        // with room for them), and each read is one of them plus an immediate.  Otherwise the
+        // compiler adds the buffer offset beside each read, one instruction over a group's budget.
+        constexpr bool kPinB = kMf >= 64 && (TB || FN % OpB::kGroupBlocks == 0);
+        constexpr int kRB = OpB::kReadBases;
+        uint32_t bb[2][kRB];
+        const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+        auto set_base = [&](int par, uint32_t b_off, int i) {
+            bb[par][i] = opb.read_base(smem_addr + b_off, i, wn * FN);
+            asm volatile("" : "+v"(bb[par][i]));
         };
-        // Load slot l of a stage's A (into A buffer pa) or B (into the B buffer at b_off);
-        // rs_a / rs_b address the stage.
+        // read unit u (< FM + FN) of k step ks: fragment u of A from A buffer pa, or fragment
+        // u - FM of B from the B buffer at b_off (whose bases are bb[bpar])
+        auto read_unit = [&](int set, int pa, uint32_t b_off, int bpar, int ks, int u) {
+            if (u < FM) {
+                fa[set][u] = opa.frag(smem + pa * A_BYTES, wm * FM + u, ks);
+            } else {
+                const int j = u - FM;
+                if constexpr (kPinB)
+                    fb[set][j] = opb.frag_at(bb[bpar][TB ? ks : j % OpB::kGroupBlocks], j, ks);
+                else
+                    fb[set][j] = opb.frag(smem + b_off, wn * FN + j, ks);
+            }
+        };
+        // Load slot l of a stage's A (into A buffer pa) or B (into the B buffer whose LDS
+        // address, plus this wave's quarter, is b_base); rs_a / rs_b address the stage.  b_base
+        // passes through an empty statement at each load, so that each load's m0 is formed in its
+        // own group rather than all of them ahead of the first.
         i32x4 rs_a, rs_b;
         auto load_a = [&](int pa, int l) { opa.load(rs_a, lds_w + (uint32_t)(pa * A_BYTES), l); };
-        auto load_b = [&](uint32_t b_off, int l) {
-            opb.load(rs_b, lds_w + (uint32_t)(kBuffers * A_BYTES) + b_off, l);
+        auto load_b = [&](uint32_t &b_base, int l) {
+            asm volatile("" : "+s"(b_base));
+            opb.load(rs_b, b_base, l);
         };
         // Prepare the resources of stage s (the cursors then move to stage s + 1).
         auto next_rsrc_a = [&](int s) { rs_a = ca.rsrc(s, nk); ca.advance(); keep_here(rs_a); keep_here(ca.base); };
@@ -943,8 +997,7 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
         // more would hold back the next 16-cycle MFMA.  The fragments of the next k step (into
         // the other set) are read at the even MFMAs of the first half; `extra` places the
         // step's resource pieces and loads.
-        constexpr int kMf = FM * FN, kUnits = FM + FN;
-        auto k_step = [&](auto set_c, int rd_pa, uint32_t rd_b, int rd_ks, auto &&extra) {
+        auto k_step = [&](auto set_c, int rd_pa, uint32_t rd_b, int rd_bpar, int rd_ks, auto &&extra) {
             constexpr int set = decltype(set_c)::value;
             // The fragments of this k step were read during the first half of the previous one:
             // one wait for all of them instead of a wait before each MFMA that uses a new one.
@@ -957,7 +1010,7 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
                 static_for<kUnits>([&](auto u_c) {
                     constexpr int u = decltype(u_c)::value;
                     constexpr int at = 2 * kUnits <= kMf ? 2 * u : (u * kMf) / kUnits;
-                    if constexpr (at == idx) read_unit(set ^ 1, rd_pa, rd_b, rd_ks, u);
+                    if constexpr (at == idx) read_unit(set ^ 1, rd_pa, rd_b, rd_bpar, rd_ks, u);
                 });
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -988,9 +1041,18 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
         uint32_t b_cur = 0, b_next = B_BYTES, b_load = 2 * B_BYTES;
         auto stage_iter = [&](int s, auto par_c) {
             constexpr int P = decltype(par_c)::value;
-            k_step(C0{}, P, b_cur, 1, [&](auto idx_c) {
+            uint32_t b_ld = lds_w + (uint32_t)(kBuffers * A_BYTES) + b_load;
+            k_step(C0{}, P, b_cur, P, 1, [&](auto idx_c) {
                 constexpr int idx = decltype(idx_c)::value;
                 if constexpr (kMf >= 64) {
+                    // the LDS base of B's loads, then the bases of the next stage's B reads
+                    if constexpr (idx == 6) asm volatile("" : "+s"(b_ld));
+                    if constexpr (kPinB) {
+                        static_for<kRB>([&](auto i_c) {
+                            if constexpr (idx == 2 * kUnits + 8 + 2 * decltype(i_c)::value)
+                                set_base(P ^ 1, b_next, decltype(i_c)::value);
+                        });
+                    }
                     static_for<4>([&](auto q_c) {
                         constexpr int q = decltype(q_c)::value;
                         if constexpr (idx == 2 * q + 1)
@@ -1002,7 +1064,7 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
                         constexpr int l = decltype(l_c)::value;
                         constexpr int span = (kMf - 10) / 2;
                         constexpr int at = 9 + 2 * ((l * span) / (kLoadsB > 1 ? kLoadsB - 1 : 1));
-                        if constexpr (at == idx) load_b(b_load, l);
+                        if constexpr (at == idx) load_b(b_ld, l);
                     });
                 } else {
                     // short k steps (smaller tiles): every piece beside the first MFMA
@@ -1012,7 +1074,7 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
                     }
                     static_for<kLoadsB>([&](auto l_c) {
                         constexpr int l = decltype(l_c)::value;
-                        if constexpr (((l * kMf) / kLoadsB + 1) % kMf == idx) load_b(b_load, l);
+                        if constexpr (((l * kMf) / kLoadsB + 1) % kMf == idx) load_b(b_ld, l);
                     });
                 }
             });
@@ -1020,7 +1082,7 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
             fix_stage(s + 1, P ^ 1, b_next);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
-            k_step(C1{}, P ^ 1, b_next, 0, [&](auto idx_c) {
+            k_step(C1{}, P ^ 1, b_next, P ^ 1, 0, [&](auto idx_c) {
                 constexpr int idx = decltype(idx_c)::value;
                 static_for<kLoadsA>([&](auto l_c) {
                     constexpr int l = decltype(l_c)::value;
@@ -1036,17 +1098,21 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
         // Prologue: stages 0 and 1 are queued; wait for stage 0.
         next_rsrc_a(0);
         next_rsrc_b(0);
+        uint32_t b_ld0 = lds_w + (uint32_t)(kBuffers * A_BYTES);
+        uint32_t b_ld1 = b_ld0 + (uint32_t)B_BYTES;
         static_for<kLoadsA>([&](auto l_c) { load_a(0, decltype(l_c)::value); });
-        static_for<kLoadsB>([&](auto l_c) { load_b(0, decltype(l_c)::value); });
+        static_for<kLoadsB>([&](auto l_c) { load_b(b_ld0, decltype(l_c)::value); });
         next_rsrc_a(1);
         next_rsrc_b(1);
         static_for<kLoadsA>([&](auto l_c) { load_a(1, decltype(l_c)::value); });
-        static_for<kLoadsB>([&](auto l_c) { load_b(B_BYTES, decltype(l_c)::value); });
+        static_for<kLoadsB>([&](auto l_c) { load_b(b_ld1, decltype(l_c)::value); });
+        if constexpr (kPinB)
+            static_for<kRB>([&](auto i_c) { set_base(0, 0u, decltype(i_c)::value); });
         wait_vmem<kLoadsPerStage>();
         fix_stage(0, 0, 0);
         __syncthreads();
     #pragma unroll
-        for (int u = 0; u < kUnits; ++u) read_unit(0, 0, 0, 0, u);
+        for (int u = 0; u < kUnits; ++u) read_unit(0, 0, 0, 0, 0, u);
 
         // Stages are taken in pairs (A buffer parity 0, then 1).  For an odd number of stages the
         // last pair's second stage lies past K: its loads read zero records, so it multiplies zeros
