@@ -986,10 +986,13 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
             StageCursor &c = p < 4 ? ca : cb;
             int &nr = p < 4 ? nr_a : nr_b;
             i32x4 &rs = p < 4 ? rs_a : rs_b;
+            // The cursor passes through an empty statement first, so that the piece's
+            // instructions are formed in its own group instead of being hoisted ahead of the step
+            // (the stage index s arrives the same way, once per stage).
             if constexpr (p % 4 == 0) { nr = s == nk - 1 ? c.last_records : 0; keep_here(nr); }
             if constexpr (p % 4 == 1) { nr = s < nk - 1 ? kNumRecords : nr; keep_here(nr); }
-            if constexpr (p % 4 == 2) { rs = c.words(nr); keep_here(rs); }
-            if constexpr (p % 4 == 3) { c.advance(); keep_here(c.base); }
+            if constexpr (p % 4 == 2) { asm volatile("" : "+s"(c.base)); rs = c.words(nr); keep_here(rs); }
+            if constexpr (p % 4 == 3) { asm volatile("" : "+s"(c.base)); c.advance(); keep_here(c.base); }
         };
 
         // One k step: the FM x FN MFMAs of fragment set `set`, each in its own fenced group with
@@ -1042,11 +1045,19 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
         auto stage_iter = [&](int s, auto par_c) {
             constexpr int P = decltype(par_c)::value;
             uint32_t b_ld = lds_w + (uint32_t)(kBuffers * A_BYTES) + b_load;
+            int s2 = s + 2;
             k_step(C0{}, P, b_cur, P, 1, [&](auto idx_c) {
                 constexpr int idx = decltype(idx_c)::value;
                 if constexpr (kMf >= 64) {
-                    // the LDS base of B's loads, then the bases of the next stage's B reads
-                    if constexpr (idx == 6) asm volatile("" : "+s"(b_ld));
+                    if constexpr (idx == 0) asm volatile("" : "+s"(s2));
+                    // the LDS base of B's loads (formed here, from an opaque copy of the buffer
+                    // offset), then the bases of the next stage's B reads
+                    if constexpr (idx == 6) {
+                        uint32_t bl = b_load;
+                        asm volatile("" : "+s"(bl));
+                        b_ld = lds_w + (uint32_t)(kBuffers * A_BYTES) + bl;
+                        asm volatile("" : "+s"(b_ld));
+                    }
                     if constexpr (kPinB) {
                         static_for<kRB>([&](auto i_c) {
                             if constexpr (idx == 2 * kUnits + 8 + 2 * decltype(i_c)::value)
@@ -1056,9 +1067,9 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
                     static_for<4>([&](auto q_c) {
                         constexpr int q = decltype(q_c)::value;
                         if constexpr (idx == 2 * q + 1)
-                            rsrc_piece(std::integral_constant<int, 4 + q>{}, s + 2);
+                            rsrc_piece(std::integral_constant<int, 4 + q>{}, s2);
                         if constexpr (idx == 2 * kUnits + 2 * q)
-                            rsrc_piece(std::integral_constant<int, q>{}, s + 2);
+                            rsrc_piece(std::integral_constant<int, q>{}, s2);
                     });
                     static_for<kLoadsB>([&](auto l_c) {
                         constexpr int l = decltype(l_c)::value;
