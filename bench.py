@@ -48,9 +48,14 @@ NUM_XCDS = 8
 DEFAULT_WORKLOAD = "bf16_8192_nn"
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(sparse: bool = False) -> str:
+    """First 16 hex digits of a SHA-256 over the sources a workload's kernel is built from: all
+    of csrc/ for the 2:4 sparse kernel, all but the sparse kernel's own files (sp24*) for the
+    dense kernels, so that a change to one family leaves the other's recorded counters valid."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "mixed_precision_dense_amd", "csrc", "*"))):
+        if not sparse and os.path.basename(p).startswith("sp24"):
+            continue
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
@@ -61,15 +66,16 @@ def counters_path(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"mpgemm_{workload}_counters.txt")
 
 
-def recorded_counters(workload: str):
-    """Figures of the committed rocprofv3 counter summary of ``workload``: a dict, or None when
-    the summary is missing or was taken on other kernel sources.
+def recorded_counters(w):
+    """Figures of the committed rocprofv3 counter summary of workload ``w``: a dict, or None
+    when the summary is missing or was taken on other kernel sources.
 
     mfma_busy_pct = SQ_VALU_MFMA_BUSY_CYCLES (summed over the chip's 1024 SIMDs) over
     1024 x (GRBM_GUI_ACTIVE summed over the 8 XCDs / 8), i.e. the share of the dispatch's
     active cycles in which an average SIMD's matrix core was busy;
     hbm_GBs = (FETCH_SIZE x fetch scale + WRITE_SIZE x write scale) x 1024 bytes over the
     rocprofv3 average kernel duration; the scales come from a plain copy of known size."""
+    workload = w.name
     path = counters_path(workload)
     if not os.path.exists(path):
         return None
@@ -79,7 +85,7 @@ def recorded_counters(workload: str):
             if "=" in line and not line.lstrip().startswith("#"):
                 key, val = line.split("=", 1)
                 kv[key.strip()] = val.strip().split()[0] if val.strip() else ""
-    if kv.get("workload") != workload or kv.get("kernel_source_sha256") != kernel_source_digest():
+    if kv.get("workload") != workload or kv.get("kernel_source_sha256") != kernel_source_digest(w.sparse24):
         return None
     try:
         busy = float(kv["sq_SQ_VALU_MFMA_BUSY_CYCLES"])
@@ -534,7 +540,7 @@ def config_record(w, args) -> dict:
     tf = w.flops / (ev["median_ms"] * 1e-3) / 1e12
     rec = {"workload": w.name, "kernel_ms_median": round(ev["median_ms"], 5),
            "TFLOPs": round(tf, 2), "pct_of_peak": round(100 * tf / pk, 2),
-           "counters": recorded_counters(w.name), "parity_full_output": parity,
+           "counters": recorded_counters(w), "parity_full_output": parity,
            "oracle_full_s": round(oracle_s, 4), "oracle_threads": oracle.num_threads(),
            "oracle_GFLOPs": round(w.flops / oracle_s / 1e9, 2)}
     if w.flops <= 2 * 256 ** 3:
@@ -588,7 +594,7 @@ def main() -> int:
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.in_type]
     unit = "TOP/s" if w.in_type == "i8" else "TFLOP/s"
-    ctr = recorded_counters(w.name)
+    ctr = recorded_counters(w)
     tile = t["tile"]
     line = {
         "metric": "TFLOP/s (TOP/s int8) and % of MI355X dense MFMA peak at 1 GPU",
