@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmpgemm.so")
 SOURCES = ["mpgemm_host.cpp", "mpgemm_api.hip", "kern_f16.hip", "kern_bf16.hip", "kern_i8.hip", "bf16x3.hip",
            "kern_fp8_fp8.hip", "kern_fp8_bf8.hip", "kern_bf8_fp8.hip", "kern_bf8_bf8.hip",
-           "sp24.hip", "sp24_fp8.hip"]
+           "sp24.hip", "sp24_f16.hip", "sp24_bf16.hip", "sp24_i8.hip", "sp24_fp8_fp8.hip",
+           "sp24_fp8_bf8.hip", "sp24_bf8_fp8.hip", "sp24_bf8_bf8.hip"]
 ARCH = "gfx950"
 
 # Packed FP32 instructions are kept out of all generated code.

@@ -1328,15 +1328,23 @@ hipError_t launch_fp8_fp8(int out, bool ta, bool tb, int tile, const Params &p, 
 hipError_t launch_fp8_bf8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
 hipError_t launch_bf8_fp8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
 hipError_t launch_bf8_bf8(int out, bool ta, bool tb, int tile, const Params &p, hipStream_t s);
-// 2:4 structured-sparse A (sp24.hip, sp24_fp8.hip): A's kept values (m x k/2, lda) in Params::A, their
-// indices (2 bits per kept value, in k order; m rows of ld_meta bytes) in meta.
+// 2:4 structured-sparse A (sp24_kernel.inc; launcher in sp24.hip, instances in sp24_<type>.hip):
+// A's kept values (m x k/2, lda) in Params::A, their indices (2 bits per kept value, in k order;
+// m rows of ld_meta bytes) in meta.
 struct SpParams {
     Params p;
     const void *meta;
     int64_t ld_meta;
 };
 hipError_t launch_sp24(int in, int out, bool tb, const SpParams &sp, hipStream_t stream);
-hipError_t launch_sp24_fp8(int in, int out, bool tb, const SpParams &sp, hipStream_t stream);
+// one input type each
+hipError_t launch_sp24_f16(int out, bool tb, const SpParams &sp, hipStream_t stream);
+hipError_t launch_sp24_bf16(int out, bool tb, const SpParams &sp, hipStream_t stream);
+hipError_t launch_sp24_i8(int out, bool tb, const SpParams &sp, hipStream_t stream);
+hipError_t launch_sp24_fp8_fp8(int out, bool tb, const SpParams &sp, hipStream_t stream);
+hipError_t launch_sp24_fp8_bf8(int out, bool tb, const SpParams &sp, hipStream_t stream);
+hipError_t launch_sp24_bf8_fp8(int out, bool tb, const SpParams &sp, hipStream_t stream);
+hipError_t launch_sp24_bf8_bf8(int out, bool tb, const SpParams &sp, hipStream_t stream);
 // BF16 pieces of an FP32 operand for the three-product GEMM (bf16x3.hip).
 hipError_t launch_split_bf16x3(const float *in, int64_t rows, int64_t cols, int64_t ld_in,
                                void *out, int64_t ld_out, bool k_along_cols, int pieces,

@@ -1,0 +1,4 @@
+// 2:4 sparse-A kernel instances for FP8 inputs: A E4M3, B E5M2 (see sp24_fp8.inc).
+#define MPG_SP_KIND IN_FP8_BF8
+#define MPG_SP_LAUNCH launch_sp24_fp8_bf8
+#include "sp24_fp8.inc"
