@@ -48,10 +48,11 @@
  * fma(alpha, acc, beta * c) in FP32.  The result is deterministic: the same inputs give the
  * same bits on every call, tile shape and launch.
  * FP8 inputs accumulate on gfx950's v_mfma_f32_16x16x128_f8f6f4, whose intermediate sums are
- * narrower (measured: blocks of 16 products in k order, about 13 fraction bits kept below each
- * block's largest exponent, each 128-deep partial sum added to the FP32 accumulator with one
- * rounding); results whose partial sums stay on that grid (small integers, for instance) are
- * exact, others carry an error up to about 2^-9 of sum |a b| per 128 k.
+ * narrower (measured: groups of 8 products keep about 13 fraction bits below the group's
+ * largest exponent, blocks of 16 products in k order are added to the FP32 accumulator in a
+ * 24-bit window and the sum rounded to FP32 after each block); results whose partial sums stay
+ * on that grid (small integers, for instance) are exact, others carry an error up to about
+ * 2^-9 of sum |a b|.
  *
  * Alignment contract (there is no slower fallback path): A, B, C (when read) and D must be
  * 16-byte aligned, and lda, ldb, ldc times the element size must be multiples of 16 bytes
