@@ -100,6 +100,45 @@ def test_fp8_bitexact_wide_range(w):
     assert model.ok, f"{model.n_bad}/{model.n} differ from the model; {model.detail}"
 
 
+def _sweep_case(t):
+    """Random configuration t of the sweep: pairing, layout, k, shape, output type, alpha,
+    beta and operand distributions (normal, uniform, log-uniform over up to 31 binades,
+    E5M2 subnormals included), dense or (every fourth) 2:4 sparse."""
+    rng = np.random.default_rng(2024 + t)
+    dists = {"e4m3": ["normal(0,1)", "log_uniform(-6,6)", "log_uniform(-9,8)", "uniform(-1,1)"],
+             "e5m2": ["normal(0,1)", "log_uniform(-12,12)", "log_uniform(-16,15)",
+                      "log_uniform(-6,6)"]}
+    fa, fb = ("e4m3", "e5m2")[rng.integers(2)], ("e4m3", "e5m2")[rng.integers(2)]
+    sparse = t % 4 == 3
+    k = int(rng.choice([16, 48, 128, 200, 384, 640, 1000, 2048]))
+    if sparse:
+        k = max(128, k // 128 * 128)
+    return Workload(f"f8sweep{t}", fa, ("f32", "bf16")[rng.integers(2)], int(rng.integers(40, 300)),
+                    int(rng.integers(40, 300)), k, transa=bool(rng.integers(2)) and not sparse,
+                    transb=bool(rng.integers(2)), b_type=fb,
+                    alpha=float(rng.choice([1.0, 0.3, -2.0])),
+                    beta=float(rng.choice([0.0, 0.5, -1.25])), a_dist=dists[fa][rng.integers(4)],
+                    b_dist=dists[fb][rng.integers(4)], c_dist="normal(0,1)", seed=900 + t,
+                    sparse24=sparse)
+
+
+@pytest.mark.parametrize("t", range(16))
+def test_fp8_bitexact_random_sweep(t):
+    from tests.gpu_harness import compare_sp24_fp8_model, run_sp24
+    w = _sweep_case(t)
+    say(f"[gpu fp8 sweep] {w.name} {'sparse ' if w.sparse24 else ''}{w.in_type}x{w.b_type}->"
+        f"{w.out_type} m={w.m} n={w.n} k={w.k} ta={w.transa} tb={w.transb} a={w.a_dist} "
+        f"b={w.b_dist} alpha={w.alpha} beta={w.beta}")
+    inp = generate(w)
+    if w.sparse24:
+        res, _ = run_sp24(inp)
+        rep = compare_sp24_fp8_model(inp, res)
+    else:
+        res = run_gpu(inp)
+        rep = compare_fp8_model(inp, res)
+    assert rep.ok, f"{rep.n_bad}/{rep.n} differ from the model; {rep.detail}"
+
+
 # GNFT-style feature-detection vectors of the FP8 instruction (the numerics page, section 3.1),
 # which fixed the model's rules: each probe is one diagonal output of a small E5M2 GEMM whose
 # A row and B column hold a few chosen power-of-two products at chosen k.  The whole output
