@@ -546,10 +546,24 @@ template <> struct Out<OUT_I32> {
 };
 
 // Map a workgroup id to its (tile_m, tile_n).  Workgroups are dispatched round-robin over
-// the 8 XCDs; ids are first remapped so that each XCD receives a contiguous run of tiles,
-// and runs are laid out in groups of kGroupM tile-rows so that the tiles of one XCD share A
-// row panels and B column panels in that XCD's L2.
+// the 8 XCDs, 32 per XCD and round of 256 tiles.  Each XCD's tiles of a round form a block of
+// 4 tile rows by 8 tile columns, so that they share A row panels and B column panels in that
+// XCD's L2 (4 + 8 panels, the least 32 whole tiles can take).  When both tile counts are
+// multiples of 16, a round's 256 tiles form a 16 x 16 region (the eight XCDs' blocks side by
+// side: 16 A and 16 B panels from beyond the L2s per round instead of 32 and 8), and the
+// regions follow each other in a serpentine, so that consecutive rounds share their A or B
+// panels in the memory-side cache.  Otherwise ids are remapped so that each XCD receives a
+// contiguous run of tiles, laid out in groups of kGroupM tile rows.
 __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int &tm, int &tn) {
+    if (tiles_m % 16 == 0 && tiles_n % 16 == 0) {
+        const int xcd = wg % 8, j = wg / 8, round = j / 32, i = j % 32;
+        const int regions_n = tiles_n / 16;
+        const int ra = round / regions_n, rb0 = round % regions_n;
+        const int rb = (ra & 1) ? regions_n - 1 - rb0 : rb0;
+        tm = 16 * ra + 4 * (xcd % 4) + i % 4;
+        tn = 16 * rb + 8 * (xcd / 4) + i / 4;
+        return;
+    }
     const int total = tiles_m * tiles_n;
     const int per_xcd = total / 8;
     int id = wg;

@@ -363,6 +363,18 @@ def test_shapes_on_one_partial_round_of_large_tiles(n):
     _assert(rep, res)
 
 
+@pytest.mark.parametrize("m,n,tile", [(4096, 8192, 256), (8192, 4096, 256), (12288, 4096, 256),
+                                      (2048, 2048, 128)])
+def test_tile_grids_of_whole_16_by_16_regions(m, n, tile):
+    """Tile grids whose sides are multiples of 16 tiles (several rounds of 16 x 16-tile regions
+    taken in a serpentine, or one region of smaller tiles): every tile written once, exactly."""
+    assert mp.mpgemm_tile_shape(m, n, "bf16") == (tile, tile)
+    w = Workload(f"regions_{m}x{n}", "bf16", "f32", m, n, 160, a_dist="int_uniform(-2,2)",
+                 b_dist="int_uniform(-2,2)", beta=0.5, c_dist="int_uniform(-4,4)", seed=61)
+    rep, res = check_case(w, exact=True)
+    _assert(rep, res)
+
+
 @pytest.mark.parametrize("entry", ["mpgemm_run", "mpgemm_run_sp24", "mpgemm_run_bf16x3"])
 def test_captured_in_a_graph_every_replay_matches_eager(entry):
     """Each entry point queued under HIP graph capture (torch.cuda.graph): the calls make no
