@@ -149,6 +149,20 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, 
                  : "memory");
 }
 
+// The same for C of a whole tile, whose every element is read once: non-temporal (the nt cache
+// policy), so that C's stream leaves the L2 and the memory-side cache to the A and B panels that
+// are read again.  D's whole-chunk stores from the LDS take the same policy (kStreamPolicy, the
+// buffer builtins' cache-policy argument) -- when rows are whole 128-byte lines: non-temporal
+// partial lines (unaligned row pitch, element-wise stores at tile edges) cost far more than the
+// default policy, under which the L2 gathers them.
+__device__ __forceinline__ void dma16_stream(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
+                 : "memory");
+}
+constexpr int kStreamPolicy = 2;   // nt
+
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima): at most N of this wave's
 // vector-memory loads are still in flight -- loads complete in order, so every older one has
 // landed (for direct-to-LDS loads: its data is in LDS).  The compiler does not insert this
@@ -769,7 +783,7 @@ __device__ __forceinline__ void store_tile_c_staged(const Params &p, AccT (&acc)
 // caller has passed a barrier after every wave's last loads and fragment reads.
 // ---------------------------------------------------------------------------------------
 template <bool kInt, int OUT, int FM, int FN, int BM, int BN, int kRegionBytes, int NW,
-          bool kReadC, typename AccT>
+          bool kReadC, bool kNT, typename AccT>
 __device__ __forceinline__ void store_full_tile_staged(const Params &p, AccT (&acc)[FM][FN],
                                                        int m0, int n0, int wm, int wn, int lane,
                                                        lds_char *region, uint32_t region_addr) {
@@ -801,7 +815,7 @@ __device__ __forceinline__ void store_full_tile_staged(const Params &p, AccT (&a
     auto load_block_row = [&](int i, int slot) {
 #pragma unroll
         for (int q = 0; q < L; ++q)
-            dma16(rc_words, chunk_off(i, q), 0u,
+            (kNT ? dma16_stream : dma16)(rc_words, chunk_off(i, q), 0u,
                   region_addr + (uint32_t)(slot * kSlotBytes + q * 1024));
     };
     // byte offset within a slot of this lane's accumulator element of row 4 g + r, block
@@ -849,7 +863,8 @@ __device__ __forceinline__ void store_full_tile_staged(const Params &p, AccT (&a
 #pragma unroll
         for (int q = 0; q < L; ++q) {
             const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(slot + q * 1024 + 16 * lane);
-            __builtin_amdgcn_raw_buffer_store_b128(v, rd, (int)chunk_off(i, q), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rd, (int)chunk_off(i, q), 0,
+                                                   kNT ? kStreamPolicy : 0);
         }
         if constexpr (kReadC && i + S < FM) {
             wait_lds<0>();                                  // the slot's values are in registers
@@ -1293,12 +1308,27 @@ __device__ __forceinline__ void gemm_tile(const Params &p, int tm, int tn, lds_c
     if (full_mn) {
         // every wave's loads and fragment reads are complete: the LDS is free
         __syncthreads();
-        if (p.read_c)
-            store_full_tile_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, NW, true>(
-                p, acc, m0, n0, wm, wn, lane_e, region, region_addr);
-        else
-            store_full_tile_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, NW, false>(
-                p, acc, m0, n0, wm, wn, lane_e, region, region_addr);
+        // C's loads and D's stores cover whole 128-byte lines when the row pitch and the
+        // pointers are line-aligned: then they stream past the caches (non-temporal); partial
+        // lines keep the default policy, under which the L2 gathers them
+        constexpr int OB = Out<OUT>::kBytes;
+        const bool lines = ((uint64_t)p.ldc * OB) % 128 == 0 &&
+                           (((uintptr_t)p.D | (p.read_c ? (uintptr_t)p.C : 0)) & 127) == 0;
+        if (p.read_c) {
+            if (lines)
+                store_full_tile_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, NW, true, true>(
+                    p, acc, m0, n0, wm, wn, lane_e, region, region_addr);
+            else
+                store_full_tile_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, NW, true, false>(
+                    p, acc, m0, n0, wm, wn, lane_e, region, region_addr);
+        } else {
+            if (lines)
+                store_full_tile_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, NW, false, true>(
+                    p, acc, m0, n0, wm, wn, lane_e, region, region_addr);
+            else
+                store_full_tile_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, NW, false, false>(
+                    p, acc, m0, n0, wm, wn, lane_e, region, region_addr);
+        }
     } else if (p.read_c) {
         __syncthreads();
         store_tile_c_staged<IN == IN_I8, OUT, FM, FN, BM, BN, kRegion, false, NW>(
