@@ -45,6 +45,7 @@ PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0, "e4m3": 5000.0,
 PEAK_HBM_GBS = 8000.0
 NUM_SIMDS = 256 * 4              # 256 CUs x 4 SIMDs
 NUM_XCDS = 8
+MAX_CLOCK_GHZ = 2.4              # MI355X peak engine clock
 DEFAULT_WORKLOAD = "bf16_8192_nn"
 
 
@@ -74,7 +75,12 @@ def recorded_counters(w):
     1024 x (GRBM_GUI_ACTIVE summed over the 8 XCDs / 8), i.e. the share of the dispatch's
     active cycles in which an average SIMD's matrix core was busy;
     hbm_GBs = (FETCH_SIZE x fetch scale + WRITE_SIZE x write scale) x 1024 bytes over the
-    rocprofv3 average kernel duration; the scales come from a plain copy of known size."""
+    rocprofv3 average kernel duration; the scales come from a plain copy of known size.
+
+    GRBM_GUI_ACTIVE counts over a window somewhat longer than the kernel itself, which matters
+    only for short kernels.  When the clock it implies over the rocprofv3 duration exceeds the
+    chip's 2.4 GHz, that window is evidently longer than the kernel: the clock is then reported
+    as null and the MFMA-busy share is marked as a lower bound."""
     workload = w.name
     path = counters_path(workload)
     if not os.path.exists(path):
@@ -94,12 +100,19 @@ def recorded_counters(w):
         traffic = float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
-    return {"file": os.path.relpath(path, ROOT),
-            "mfma_busy_pct": round(100.0 * busy / (NUM_SIMDS * active), 2),
-            "hbm_GBs": round(traffic / (dur_ns * 1e-9) / 1e9, 1),
-            "hbm_bytes_per_launch": traffic,
-            "rocprof_avg_us": round(dur_ns / 1e3, 2),
-            "clock_GHz_from_counters": round(active / dur_ns, 3)}
+    clock = active / dur_ns
+    rec = {"file": os.path.relpath(path, ROOT),
+           "mfma_busy_pct": round(100.0 * busy / (NUM_SIMDS * active), 2),
+           "hbm_GBs": round(traffic / (dur_ns * 1e-9) / 1e9, 1),
+           "hbm_bytes_per_launch": traffic,
+           "rocprof_avg_us": round(dur_ns / 1e3, 2),
+           "clock_GHz_from_counters": round(clock, 3) if clock <= MAX_CLOCK_GHZ else None}
+    if clock > MAX_CLOCK_GHZ:
+        rec["counter_window_note"] = (
+            f"GRBM_GUI_ACTIVE over the kernel's duration implies {clock:.2f} GHz, above the "
+            f"chip's {MAX_CLOCK_GHZ} GHz: the counted window is longer than this short kernel, "
+            "so mfma_busy_pct is a lower bound")
+    return rec
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
@@ -636,6 +649,8 @@ def main() -> int:
             "file": ctr["file"], "rocprof_avg_us": ctr["rocprof_avg_us"],
             "frac_from_rocprof_avg": round(flops / (ctr["rocprof_avg_us"] * 1e-6) / 1e12 / peak, 4),
             "clock_GHz_from_counters": ctr["clock_GHz_from_counters"]}
+        if "counter_window_note" in ctr:
+            line["counters"]["counter_window_note"] = ctr["counter_window_note"]
     if w.sparse24:
         # the work is the kept products (2 m n k/2); the dense GEMM of the same shape would be
         # twice that

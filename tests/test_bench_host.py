@@ -72,6 +72,21 @@ def test_counters_are_read_only_for_their_workload_and_sources(tree):
     assert bench.recorded_counters(WORKLOADS["i8_4096_nn"]) is None   # no file at all
 
 
+def test_an_impossible_counter_clock_is_not_reported(tree):
+    # GRBM_GUI_ACTIVE counts a window around the dispatch; over a short kernel's duration it
+    # can imply more than the chip's 2.4 GHz, and then the clock is withheld and the busy
+    # share flagged as a lower bound
+    w = WORKLOADS["f16_5000x3000x1000_f16out"]
+    _write_counters(tree, w, bench.kernel_source_digest(), active=8 * 2.6e3 * 34.6, avg_ns=34.6e3)
+    c = bench.recorded_counters(w)
+    assert c["clock_GHz_from_counters"] is None
+    assert "lower bound" in c["counter_window_note"] and "2.60 GHz" in c["counter_window_note"]
+    _write_counters(tree, w, bench.kernel_source_digest(), active=8 * 2.3e3 * 34.6, avg_ns=34.6e3)
+    c = bench.recorded_counters(w)
+    assert c["clock_GHz_from_counters"] == pytest.approx(2.3, abs=1e-3)
+    assert "counter_window_note" not in c
+
+
 def test_sparse_counters_use_the_sparse_digest(tree):
     w = NEXT_WORKLOADS["f16_sp24_4096_nt"]
     _write_counters(tree, w, bench.kernel_source_digest())
