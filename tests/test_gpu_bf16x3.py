@@ -6,7 +6,8 @@ section 5.1).
     padding included, for every layout;
   * D equals the oracle's block model of the three-product GEMM bit for bit, and lies within
     the method's bound of the double-precision FP32 GEMM;
-  * ragged k (pieces padded to multiples of 8), tile edges, the benchmark workload (sampled),
+  * ragged k (pieces padded to multiples of 8), tile edges, the benchmark workload (the model
+    at sampled points, the bound at every output),
     Inf/NaN/overflowing/subnormal inputs, k = 0, D == C, and the workspace contract.
 """
 import numpy as np
@@ -80,6 +81,26 @@ def test_bf16x3_workload_sampled():
     w = Workload("f32_4096_nt_bf16x3", "f32", "f32", 4096, 4096, 4096, transb=True,
                  a_dist="normal(0,1)", b_dist="normal(0,1)", seed=6)
     _check(w, points=sample_points(w.m, w.n, 2000))
+
+
+def test_bf16x3_workload_every_output_within_bound():
+    """Every output of the 4096^3 workload against the double-precision FP32 GEMM, within the
+    three-product bound (the block model is compared at sampled points above: over all 16.7 M
+    outputs its 12288-term sums would keep the oracle busy for minutes)."""
+    w = Workload("f32_4096_nt_bf16x3", "f32", "f32", 4096, 4096, 4096, transb=True,
+                 a_dist="normal(0,1)", b_dist="normal(0,1)", seed=6)
+    say(f"[gpu bf16x3] {w.name} every output against the FP32 GEMM in double")
+    inp = generate(w)
+    res, _, _ = run_bf16x3(inp)
+    assert res.guard_ok
+    v, S = oracle.gemm_f32(w.transa, w.transb, w.m, w.n, w.k, w.alpha, inp.A, w.lda, inp.B,
+                           w.ldb, w.beta, inp.C, w.ldc)
+    bc = w.beta * inp.C[:, : w.n].astype(np.float64) if w.beta else np.zeros_like(v)
+    D = np.asarray(res.D[:, : w.n], np.float64)
+    assert np.all(np.isfinite(D)) and np.all(np.isfinite(v))
+    ratio = np.abs(D - v) / oracle.bf16x3_bound(S, w.k, w.alpha, bc)
+    say(f"[gpu bf16x3] worst error / bound over {ratio.size} outputs: {ratio.max():.3g}")
+    assert ratio.max() <= 1.0
 
 
 @pytest.mark.parametrize("dist", ["log_uniform(-60,60)", "log_uniform(-140,-100)"])
