@@ -439,3 +439,47 @@ def test_captured_in_a_graph_every_replay_matches_eager(entry):
         torch.cuda.synchronize()
         assert torch.equal(dD.view(torch.int32), want.view(torch.int32))
     say(f"[gpu case] graph capture of {entry}: 4 replays bit-identical to the eager call")
+
+
+@pytest.mark.parametrize("in_type,out_type", [("f16", "f32"), ("bf16", "bf16")])
+def test_line_alignment_of_c_and_d_changes_no_bit(in_type, out_type):
+    """Whole tiles: C and D stream past the caches only when the row pitch and both pointers
+    lie on 128-byte lines, otherwise they take the default cache policy.  C and D placed on a
+    line or 16, 48 or 80 bytes past one give the same bits, equal to the block-FMA model, and
+    leave the bytes around D untouched."""
+    from tests.gpu_harness import GUARD_ROWS, SENTINEL, GpuResult, compare_model
+    w = Workload(f"align_{in_type}_{out_type}", in_type, out_type, 512, 768, 320, beta=0.5,
+                 alpha=1.5, a_dist="normal(0,1)", b_dist="normal(0,1)", c_dist="normal(0,1)",
+                 seed=91)
+    inp = generate(w)
+    ob = np.dtype(np.float32 if out_type == "f32" else np.uint16).itemsize
+    nbytes = w.m * w.ldc * ob
+    guard = GUARD_ROWS * w.ldc * ob
+    assert (w.ldc * ob) % 128 == 0                       # the row pitch itself is whole lines
+    dA, dB = mp.device_buffer(inp.A, in_type), mp.device_buffer(inp.B, in_type)
+    c_bytes = torch.from_numpy(np.ascontiguousarray(inp.C).view(np.uint8).reshape(-1))
+    first = None
+    for c_off, d_off in [(0, 0), (16, 0), (0, 16), (48, 80)]:
+        say(f"[gpu case] {w.name} m={w.m} n={w.n} k={w.k} C at line + {c_off} B, "
+            f"D at line + {d_off} B")
+        craw = torch.zeros(nbytes + 256, dtype=torch.uint8, device="cuda")
+        cs = (-craw.data_ptr()) % 128 + c_off
+        craw[cs: cs + nbytes].copy_(c_bytes)
+        draw = torch.full((nbytes + guard + 512,), SENTINEL, dtype=torch.uint8, device="cuda")
+        ds = (-draw.data_ptr()) % 128 + 128 + d_off       # 128 or more sentinel bytes before D
+        mp.mpgemm_run(handle().h, w.transa, w.transb, w.m, w.n, w.k, w.alpha, dA, in_type,
+                      w.lda, dB, in_type, w.ldb, w.beta, craw.data_ptr() + cs, out_type, w.ldc,
+                      draw.data_ptr() + ds, "f32")
+        torch.cuda.synchronize()
+        raw = draw.cpu().numpy()
+        assert np.all(raw[:ds] == SENTINEL) and np.all(raw[ds + nbytes:] == SENTINEL)
+        assert np.array_equal(craw[cs: cs + nbytes].cpu(), c_bytes)   # C is only read
+        D = raw[ds: ds + nbytes].copy()
+        if first is None:
+            first = D
+            storage = np.float32 if out_type == "f32" else np.uint16
+            res = GpuResult(D=D.view(storage).reshape(w.m, w.ldc), guard_ok=True)
+            rep = compare_model(inp, res)
+            assert rep.ok, f"{rep.n_bad}/{rep.n} differ from the model; {rep.detail}"
+        else:
+            assert np.array_equal(D, first), "a C or D placement changed the result"
