@@ -87,6 +87,17 @@ def test_encode_f16_tie_table():
     assert oracle.encode_rne(float("nan"), "f16") & 0x7C00 == 0x7C00
 
 
+def test_encode_nan_is_the_quiet_nan_with_its_sign():
+    """A NaN encodes as the exponent field all ones with only the leading fraction bit set (the
+    quiet NaN of IEEE 754, section 6.2.1), keeping the sign: not as an infinity."""
+    for fmt, (e, m) in {"f16": (5, 10), "bf16": (8, 7), "f32": (8, 23)}.items():
+        quiet = (((1 << e) - 1) << m) | (1 << (m - 1))
+        assert oracle.encode_rne(float("nan"), fmt) == quiet, fmt
+        assert oracle.encode_rne(-float("nan"), fmt) == quiet | (1 << (e + m)), fmt
+    assert oracle.encode_rne(float("nan"), "f16") == int(np.array(np.nan, np.float16).view(np.uint16))
+    assert oracle.encode_rne(float("nan"), "f32") == int(np.array(np.nan, np.float32).view(np.uint32))
+
+
 def test_encode_f32_vs_numpy():
     rng = np.random.default_rng(12)
     vals = np.concatenate([

@@ -254,6 +254,9 @@ RULES = [
     # ... and toward minus infinity for a negative sum: -(2^8 + 2^-16 + 2^-24) cut at 2^-23
     # grows to -(2^8 + 2^-16 + 2^-23), still beyond the tie: -(2^8 + 2^-15).
     ("negative sum cut", [(0, 16.0, -16.0), (1, 2.0 ** -8, 2.0 ** -8)] + PAIR + [(10, 2.0 ** -8, -(2.0 ** -7)), (11, T12 / 2, -(2.0 ** -11))], -(256.0 + 2.0 ** -15)),
+    # A block whose products are all zero (a zero operand in each) leaves the running sum as
+    # it is: 1 + 2^-23 from the first block survives the second.
+    ("zero block", [(0, 1.0, 1.0), (1, T12, T12), (2, T12, T12), (8, 0.0, 4.0), (9, 2.0, 0.0)], 1.0 + 2.0 ** -23),
     # Specials: Inf x 0 and opposite infinities are NaN, in one block or across blocks.
     ("inf", [(0, INF, 1.0)], INF),
     ("inf x 0", [(0, INF, 0.0)], NAN),
