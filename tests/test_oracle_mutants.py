@@ -1,0 +1,144 @@
+"""The plain oracle's and the FP16/BF16 block model's pins catch mistakes: each planted mistake
+below -- an operand read transposed, a dropped term or scale, a wrong rounding or cut
+direction, a misplaced window, a wrong block size -- makes at least one pin fail.  Code
+mistakes are planted in one function of a copy of the oracle's C source, built with gcc (the
+oracle loads it through MPGEMM_ORACLE_LIB); parameter mistakes are passed to the model's entry
+point.  CPU only."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "mpgemm_oracle.c")
+GEMM = ["tests/test_oracle_gemm.py"]
+FORMATS = ["tests/test_oracle_formats.py"]
+MODEL = ["tests/test_oracle_mfma_model.py"]
+
+# name: (function the mistake is planted in, original text, planted text, pin files)
+CODE = {
+    "A's transpose flag read the wrong way": (
+        "static int64_t a_index(", "return transa ? p * lda + i : i * lda + p;",
+        "return transa ? i * lda + p : p * lda + i;", GEMM),
+    "B's transpose flag read the wrong way": (
+        "static int64_t b_index(", "return transb ? j * ldb + p : p * ldb + j;",
+        "return transb ? p * ldb + j : j * ldb + p;", GEMM),
+    "beta * c dropped": (
+        "static void fp_point(", "        out = alpha * s + betac;", "        out = alpha * s;",
+        GEMM),
+    "alpha dropped when beta is zero": (
+        "static void fp_point(", "        out = alpha * s;\n", "        out = s;\n", GEMM),
+    "the bound's sum not of magnitudes": (
+        "static void fp_point(", "        sa += fabs(prod);", "        sa += prod;", GEMM),
+    "the last product left out": (
+        "static void fp_point(", "for (int64_t p = 0; p < k; ++p)",
+        "for (int64_t p = 0; p < k - 1; ++p)", GEMM),
+    "INT8 alpha dropped": (
+        "static uint64_t int_point(", "uint64_t out = (uint64_t)alpha * (uint64_t)s;",
+        "uint64_t out = (uint64_t)s;", GEMM),
+    "INT8 beta * c dropped": (
+        "static uint64_t int_point(",
+        "        out += (uint64_t)beta * (uint64_t)(int64_t)C[i * ldc + j];", "        out += 0;",
+        GEMM),
+    "INT8 bytes read as unsigned": (
+        "static uint64_t int_point(", "s += (int64_t)A[a_index(transa, lda, i, p)]",
+        "s += (int64_t)(uint8_t)A[a_index(transa, lda, i, p)]", GEMM),
+    "INT8 result saturated instead of wrapped": (
+        "static uint64_t int_point(", "    return out;",
+        "    return (uint64_t)((int64_t)out > 2147483647 ? 2147483647\n"
+        "        : (int64_t)out < -2147483647 - 1 ? -2147483647 - 1 : (int64_t)out);", GEMM),
+    "ties rounded away from zero": (
+        "uint64_t oracle_encode_rne(", "    if (frac > 0.5 || (frac == 0.5 && (r & 1)))",
+        "    if (frac >= 0.5)", FORMATS),
+    "no overflow to infinity": (
+        "uint64_t oracle_encode_rne(", "    if (x > bias)", "    if (0)", FORMATS),
+    "NaN encoded as an infinity": (
+        "uint64_t oracle_encode_rne(",
+        "        return sbit | (emax_field << mbits) | (1ull << (mbits - 1));",
+        "        return sbit | (emax_field << mbits);", FORMATS),
+    "subnormals decoded one binade low": (
+        "double oracle_decode(", "        mag = ldexp((double)f, 1 - bias - mbits);",
+        "        mag = ldexp((double)f, -bias - mbits);", FORMATS),
+    "model: products cut toward minus infinity": (
+        "static float mfma_block(",
+        "        const i128 term = sh >= 0 ? (pm << sh) : cut_toward_zero(pm, -sh);\n"
+        "        S += (a[t].neg ^ b[t].neg) ? -term : term;",
+        "        const i128 sp = (a[t].neg ^ b[t].neg) ? -pm : pm;\n"
+        "        S += sh >= 0 ? sp * ((i128)1 << sh) : cut_floor(sp, -sh);", MODEL),
+    "model: products rounded to nearest": (
+        "static float mfma_block(", "(pm << sh) : cut_toward_zero(pm, -sh);",
+        "(pm << sh) : cut_toward_zero(pm + (((i128)1 << (-sh)) >> 1), -sh);", MODEL),
+    "model: running value cut toward zero": (
+        "static float mfma_block(", "cut_floor(sM, -sa);", "cut_toward_zero(sM, -sa);", MODEL),
+    "model: sum width cut toward zero": (
+        "static float mfma_block(", "S = cut_floor(S, drop)", "S = cut_toward_zero(S, drop)",
+        MODEL),
+    "model: sum width one bit short": (
+        "static float mfma_block(", "const int drop = lead - (sum_bits - 1) - g;",
+        "const int drop = lead - sum_bits - g;", MODEL),
+    "model: aligned to the smallest exponent": (
+        "static float mfma_block(", "if (!have || e > emax)", "if (!have || e < emax)", MODEL),
+    "model: Inf times zero not NaN": (
+        "static float mfma_block(", "            if (other_zero)\n                nan = 1;",
+        "            if (0)\n                nan = 1;", MODEL),
+    "model: a block of zero products clears the running value": (
+        "static float mfma_block(", "    if (!have)\n        return acc;",
+        "    if (!have)\n        return 0.0f;", MODEL),
+    "model: FP32 result cut instead of rounded": (
+        "static float fp32_from_scaled(", "        if (rem > half || (rem == half && (u & 1)))",
+        "        if (0)", MODEL),
+    "model: subnormal operands one binade low": (
+        "static fp_parts parts16(", "        p.expo = (int16_t)(1 - bias);",
+        "        p.expo = (int16_t)(-bias);", MODEL),
+    "model: epilogue rounds twice": (
+        "static float mfma_epilogue(",
+        "    return fmaf(alpha, acc, beta * elem_f32(C, ctype, i * ldc + j));",
+        "    return alpha * acc + beta * elem_f32(C, ctype, i * ldc + j);", MODEL),
+}
+PARAMS = {"blocks of 4": dict(nblk=4), "blocks of 16": dict(nblk=16),
+          "a 23-bit window": dict(frac=23), "a 25-bit window": dict(frac=25),
+          "a 31-bit sum": dict(sum_bits=31), "a 33-bit sum": dict(sum_bits=33),
+          "no sum width": dict(sum_bits=0)}
+
+
+def _pins_fail(files, env=None, prelude=""):
+    code = (prelude + "import sys, pytest\n"
+            f"sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider'] + {files!r}))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=300)
+    return r.returncode == 1 and " failed" in r.stdout
+
+
+def _plant(src, fn, old, new):
+    """src with the first `old` inside function `fn` (from its header to its closing brace)
+    replaced by `new`."""
+    start = src.index(fn)
+    end = src.index("\n}\n", start)
+    pos = src.index(old, start)
+    assert pos + len(old) <= end, "the planted text must lie inside the function"
+    return src[:pos] + new + src[pos + len(old):]
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc builds the mutated oracle")
+@pytest.mark.parametrize("name", sorted(CODE))
+def test_code_mistake_fails_a_pin(name, tmp_path):
+    fn, old, new, pins = CODE[name]
+    path = tmp_path / "mutant.c"
+    path.write_text(_plant(open(SRC).read(), fn, old, new))
+    so = tmp_path / "mutant.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+                    "-fPIC", "-shared", "-o", str(so), str(path), "-lm"], check=True)
+    assert _pins_fail(pins, dict(os.environ, MPGEMM_ORACLE_LIB=str(so))), name
+
+
+@pytest.mark.parametrize("name", sorted(PARAMS))
+def test_model_parameter_mistake_fails_a_pin(name):
+    prelude = ("import functools, oracle\n"
+               f"oracle.gemm_mfma = functools.partial(oracle.gemm_mfma, **{PARAMS[name]!r})\n")
+    assert _pins_fail(MODEL, prelude=prelude), name
+
+
+def test_the_unmutated_oracle_passes_its_pins():
+    assert not _pins_fail(GEMM + FORMATS + MODEL)
