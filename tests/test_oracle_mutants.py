@@ -1,6 +1,7 @@
-"""The plain oracle's and the FP16/BF16 block model's pins catch mistakes: each planted mistake
-below -- an operand read transposed, a dropped term or scale, a wrong rounding or cut
-direction, a misplaced window, a wrong block size -- makes at least one pin fail.  Code
+"""The pins of the plain oracle, the FP16/BF16 block model, the 2:4 sparse oracle and the BF16
+split catch mistakes: each planted mistake below -- an operand read transposed, a dropped term
+or scale, a wrong rounding or cut direction, a misplaced window, a wrong block size, metadata
+read the wrong way, a piece cut instead of rounded -- makes at least one pin fail.  Code
 mistakes are planted in one function of a copy of the oracle's C source, built with gcc (the
 oracle loads it through MPGEMM_ORACLE_LIB); parameter mistakes are passed to the model's entry
 point.  CPU only."""
@@ -16,6 +17,8 @@ SRC = os.path.join(ROOT, "oracle", "mpgemm_oracle.c")
 GEMM = ["tests/test_oracle_gemm.py"]
 FORMATS = ["tests/test_oracle_formats.py"]
 MODEL = ["tests/test_oracle_mfma_model.py"]
+SP24 = ["tests/test_oracle_sp24.py"]
+SPLIT = ["tests/test_oracle_bf16x3.py"]
 
 # name: (function the mistake is planted in, original text, planted text, pin files)
 CODE = {
@@ -96,6 +99,24 @@ CODE = {
         "static float mfma_epilogue(",
         "    return fmaf(alpha, acc, beta * elem_f32(C, ctype, i * ldc + j));",
         "    return alpha * acc + beta * elem_f32(C, ctype, i * ldc + j);", MODEL),
+    "sparse: positions read from the metadata byte's high bits": (
+        "static void sp24_point(", "(2 * (j % 4))", "(6 - 2 * (j % 4))", SP24),
+    "sparse: kept values placed in the wrong group of four": (
+        "static void sp24_point(", "const int64_t kk = 4 * (j / 2) + idx;",
+        "const int64_t kk = 4 * (j / 4) + idx;", SP24),
+    "sparse model: positions read from the high bits": (
+        "int oracle_gemm_sp24_mfma_points(", "(2 * (j % 4))", "(6 - 2 * (j % 4))", SP24),
+    "sparse INT8: positions read from the high bits": (
+        "int oracle_gemm_sp24_int_points(", "(2 * (j % 4))", "(6 - 2 * (j % 4))", SP24),
+    "split: high piece cut instead of rounded": (
+        "int oracle_split_bf16(", "const uint64_t h = oracle_encode_rne(v, 8, 7);",
+        "const uint64_t h = (union { float f; uint32_t u; }){ (float)v }.u >> 16;", SPLIT),
+    "split: low piece taken from x, not x - x_hi": (
+        "int oracle_split_bf16(", "oracle_encode_rne(v - hv, 8, 7)", "oracle_encode_rne(v, 8, 7)",
+        SPLIT),
+    "split: low piece cut instead of rounded": (
+        "int oracle_split_bf16(", "(uint16_t)oracle_encode_rne(v - hv, 8, 7)",
+        "(uint16_t)((union { float f; uint32_t u; }){ (float)(v - hv) }.u >> 16)", SPLIT),
 }
 PARAMS = {"blocks of 4": dict(nblk=4), "blocks of 16": dict(nblk=16),
           "a 23-bit window": dict(frac=23), "a 25-bit window": dict(frac=25),
@@ -141,4 +162,4 @@ def test_model_parameter_mistake_fails_a_pin(name):
 
 
 def test_the_unmutated_oracle_passes_its_pins():
-    assert not _pins_fail(GEMM + FORMATS + MODEL)
+    assert not _pins_fail(GEMM + FORMATS + MODEL + SP24 + SPLIT)
