@@ -1,7 +1,8 @@
 """The pins of the plain oracle, the FP16/BF16 block model, the 2:4 sparse oracle and the BF16
 split catch mistakes: each planted mistake below -- an operand read transposed, a dropped term
 or scale, a wrong rounding or cut direction, a misplaced window, a wrong block size, metadata
-read the wrong way, a piece cut instead of rounded -- makes at least one pin fail.  Code
+read the wrong way, a piece cut instead of rounded, an FP8 format misread -- makes at least
+one pin fail.  Code
 mistakes are planted in one function of a copy of the oracle's C source, built with gcc (the
 oracle loads it through MPGEMM_ORACLE_LIB); parameter mistakes are passed to the model's entry
 point.  CPU only."""
@@ -19,6 +20,7 @@ FORMATS = ["tests/test_oracle_formats.py"]
 MODEL = ["tests/test_oracle_mfma_model.py"]
 SP24 = ["tests/test_oracle_sp24.py"]
 SPLIT = ["tests/test_oracle_bf16x3.py"]
+FP8 = ["tests/test_oracle_fp8.py"]
 
 # name: (function the mistake is planted in, original text, planted text, pin files)
 CODE = {
@@ -117,6 +119,14 @@ CODE = {
     "split: low piece cut instead of rounded": (
         "int oracle_split_bf16(", "(uint16_t)oracle_encode_rne(v - hv, 8, 7)",
         "(uint16_t)((union { float f; uint32_t u; }){ (float)(v - hv) }.u >> 16)", SPLIT),
+    "E4M3 with IEEE-style infinities": (
+        "double oracle_decode_e4m3(", "    if (e == 15 && f == 7)\n        mag = NAN;",
+        "    if (e == 15)\n        mag = f ? NAN : INFINITY;", FP8),
+    "E4M3 subnormals one binade low": (
+        "double oracle_decode_e4m3(", "mag = ldexp((double)f, 1 - 7 - 3);",
+        "mag = ldexp((double)f, -7 - 3);", FP8),
+    "E5M2 read with E4M3's fields": (
+        "static double decode8(", "oracle_decode(bits, 5, 2)", "oracle_decode_e4m3(bits)", FP8),
 }
 PARAMS = {"blocks of 4": dict(nblk=4), "blocks of 16": dict(nblk=16),
           "a 23-bit window": dict(frac=23), "a 25-bit window": dict(frac=25),
@@ -162,4 +172,4 @@ def test_model_parameter_mistake_fails_a_pin(name):
 
 
 def test_the_unmutated_oracle_passes_its_pins():
-    assert not _pins_fail(GEMM + FORMATS + MODEL + SP24 + SPLIT)
+    assert not _pins_fail(GEMM + FORMATS + MODEL + SP24 + SPLIT + FP8)
