@@ -1,11 +1,10 @@
-"""The pins of the plain oracle, the FP16/BF16 block model, the 2:4 sparse oracle and the BF16
-split catch mistakes: each planted mistake below -- an operand read transposed, a dropped term
-or scale, a wrong rounding or cut direction, a misplaced window, a wrong block size, metadata
-read the wrong way, a piece cut instead of rounded, an FP8 format misread -- makes at least
-one pin fail.  Code
-mistakes are planted in one function of a copy of the oracle's C source, built with gcc (the
-oracle loads it through MPGEMM_ORACLE_LIB); parameter mistakes are passed to the model's entry
-point.  CPU only."""
+"""The pins of the plain oracle, the FP16/BF16 block model, the 2:4 sparse oracle, the BF16
+split and the FP8 decoders catch mistakes: each planted mistake below -- an operand read
+transposed, a dropped term or scale, a wrong rounding or cut direction, a misplaced window, a
+wrong block size, metadata read the wrong way, a piece cut instead of rounded, an FP8 format
+misread -- makes at least one pin fail.  Code mistakes are planted in one function of a copy
+of the oracle's C source, built with gcc (the oracle loads it through MPGEMM_ORACLE_LIB);
+parameter mistakes are passed to the model's entry point.  CPU only."""
 import os
 import shutil
 import subprocess
