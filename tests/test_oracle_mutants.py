@@ -5,15 +5,12 @@ wrong block size, metadata read the wrong way, a piece cut instead of rounded, a
 misread -- makes at least one pin fail.  Code mistakes are planted in one function of a copy
 of the oracle's C source, built with gcc (the oracle loads it through MPGEMM_ORACLE_LIB);
 parameter mistakes are passed to the model's entry point.  CPU only."""
-import os
 import shutil
-import subprocess
-import sys
 
 import pytest
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "oracle", "mpgemm_oracle.c")
+from tests.planted import pins_fail, survivors
+
 GEMM = ["tests/test_oracle_gemm.py"]
 FORMATS = ["tests/test_oracle_formats.py"]
 MODEL = ["tests/test_oracle_mfma_model.py"]
@@ -133,42 +130,16 @@ PARAMS = {"blocks of 4": dict(nblk=4), "blocks of 16": dict(nblk=16),
           "no sum width": dict(sum_bits=0)}
 
 
-def _pins_fail(files, env=None, prelude=""):
-    code = (prelude + "import sys, pytest\n"
-            f"sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider'] + {files!r}))\n")
-    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
-                       text=True, timeout=300)
-    return r.returncode == 1 and " failed" in r.stdout
-
-
-def _plant(src, fn, old, new):
-    """src with the first `old` inside function `fn` (from its header to its closing brace)
-    replaced by `new`."""
-    start = src.index(fn)
-    end = src.index("\n}\n", start)
-    pos = src.index(old, start)
-    assert pos + len(old) <= end, "the planted text must lie inside the function"
-    return src[:pos] + new + src[pos + len(old):]
+def _model_params(kw):
+    return ("import functools, oracle\n"
+            f"oracle.gemm_mfma = functools.partial(oracle.gemm_mfma, **{kw!r})\n")
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc builds the mutated oracle")
-@pytest.mark.parametrize("name", sorted(CODE))
-def test_code_mistake_fails_a_pin(name, tmp_path):
-    fn, old, new, pins = CODE[name]
-    path = tmp_path / "mutant.c"
-    path.write_text(_plant(open(SRC).read(), fn, old, new))
-    so = tmp_path / "mutant.so"
-    subprocess.run(["gcc", "-O1", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-                    "-fPIC", "-shared", "-o", str(so), str(path), "-lm"], check=True)
-    assert _pins_fail(pins, dict(os.environ, MPGEMM_ORACLE_LIB=str(so))), name
-
-
-@pytest.mark.parametrize("name", sorted(PARAMS))
-def test_model_parameter_mistake_fails_a_pin(name):
-    prelude = ("import functools, oracle\n"
-               f"oracle.gemm_mfma = functools.partial(oracle.gemm_mfma, **{PARAMS[name]!r})\n")
-    assert _pins_fail(MODEL, prelude=prelude), name
+def test_every_planted_mistake_fails_a_pin():
+    params = {name: (kw, MODEL) for name, kw in PARAMS.items()}
+    assert survivors(CODE, params, _model_params) == []
 
 
 def test_the_unmutated_oracle_passes_its_pins():
-    assert not _pins_fail(GEMM + FORMATS + MODEL + SP24 + SPLIT + FP8)
+    assert not pins_fail(GEMM + FORMATS + MODEL + SP24 + SPLIT + FP8)
