@@ -141,6 +141,45 @@ def test_half_output_bound_and_exact_mode():
     assert not oracle.check_fp(wrong, "f16", ref, w.k, 1.0, exact=True).ok
 
 
+
+def test_beta_c_rounded_to_fp32_passes():
+    """beta * c rounded to FP32 before the add: with products near 2^-21 beside |beta c| near
+    0.1, that rounding is the error, and the bound's 2^-23 |beta c| term must admit it."""
+    w = Workload("cmp_bc", "f16", "f32", 16, 16, 1, beta=float(np.float32(0.1)),
+                 a_dist="log_uniform(-12,-10)", b_dist="log_uniform(-12,-10)",
+                 c_dist="normal(0,1)", seed=24)
+    inp = generate(w)
+    ref = oracle.gemm_fp(False, False, w.m, w.n, w.k, w.alpha, inp.A, "f16", w.lda, inp.B, "f16",
+                         w.ldb, w.beta, inp.C, "f32", w.ldc)
+    a, b, c = _decoded(inp)
+    D = _epilogue(_f32_accumulate(a, b, "forward"), w, c)
+    assert not np.array_equal(D.astype(np.float64), ref.v)   # the rounding is there to admit
+    rep = oracle.check_fp(D, "f32", ref, w.k, w.alpha)
+    assert rep.ok, rep.detail
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_16bit_outputs_rounded_once_pass(fmt):
+    """An FP32 accumulation rounded once to FP16 or BF16 output passes the bound check (the
+    output rounding, 2^-11 or 2^-8 of |v|, dwarfs the short sum's K 2^-23 S)."""
+    w = Workload(f"cmp_o_{fmt}", fmt, fmt, 16, 16, 4, a_dist="normal(0,1)", b_dist="normal(0,1)",
+                 seed=25)
+    inp = generate(w)
+    ref = oracle.gemm_fp(False, False, w.m, w.n, w.k, 1.0, inp.A, fmt, w.lda, inp.B, fmt, w.ldb,
+                         0.0, None, fmt, w.ldc)
+    a, b, _ = _decoded(inp)
+    D = oracle.round_to(_f32_accumulate(a, b, "forward").astype(np.float64), fmt)
+    rep = oracle.check_fp(D, fmt, ref, w.k, 1.0)
+    assert rep.ok, rep.detail
+    assert rep.worst_ratio > 0.01                  # the output rounding carries real weight
+
+
+def test_exact_mode_takes_nan_as_equal_to_nan():
+    ref = oracle.FpReference(v=np.array([np.nan, 1.0]), S=np.ones(2), bc=np.zeros(2))
+    assert oracle.check_fp(np.array([np.nan, 1.0], np.float32), "f32", ref, 1, 1.0, exact=True).ok
+    assert not oracle.check_fp(np.array([1.0, 1.0], np.float32), "f32", ref, 1, 1.0, exact=True).ok
+
+
 def test_nonfinite_rules():
     ref = oracle.FpReference(v=np.array([np.nan, np.inf, -np.inf, 1.0]), S=np.array([1.0] * 4),
                              bc=np.zeros(4))
