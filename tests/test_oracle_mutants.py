@@ -2,9 +2,10 @@
 split and the FP8 decoders catch mistakes: each planted mistake below -- an operand read
 transposed, a dropped term or scale, a wrong rounding or cut direction, a misplaced window, a
 wrong block size, metadata read the wrong way, a piece cut instead of rounded, an FP8 format
-misread -- makes at least one pin fail.  Code mistakes are planted in one function of a copy
-of the oracle's C source, built with gcc (the oracle loads it through MPGEMM_ORACLE_LIB);
-parameter mistakes are passed to the model's entry point.  CPU only."""
+misread, a comparator that admits or rejects too much -- makes at least one pin fail.  Code
+mistakes are planted in one function of a copy of the oracle's C source, built with gcc (the
+oracle loads it through MPGEMM_ORACLE_LIB), or in the source of one function of its Python
+part; parameter mistakes are passed to the model's entry point.  CPU only."""
 import shutil
 
 import pytest
@@ -17,6 +18,7 @@ MODEL = ["tests/test_oracle_mfma_model.py"]
 SP24 = ["tests/test_oracle_sp24.py"]
 SPLIT = ["tests/test_oracle_bf16x3.py"]
 FP8 = ["tests/test_oracle_fp8.py"]
+COMPARE = ["tests/test_compare.py"]
 
 # name: (function the mistake is planted in, original text, planted text, pin files)
 CODE = {
@@ -130,6 +132,48 @@ PARAMS = {"blocks of 4": dict(nblk=4), "blocks of 16": dict(nblk=16),
           "no sum width": dict(sum_bits=0)}
 
 
+# name: ((function of oracle/__init__.py, original text, planted text), pin files): the
+# function's source is edited and run again in the oracle module before the pins
+PYTHON = {
+    "bound without beta * c's rounding": (
+        ("fp_bound", "E = a * keff * 2.0 ** -23 * ref.S + 2.0 ** -23 * np.abs(ref.bc)",
+         "E = a * keff * 2.0 ** -23 * ref.S"), COMPARE),
+    "bound 2^10 too loose": (
+        ("fp_bound", "E = a * keff * 2.0 ** -23 * ref.S", "E = a * keff * 2.0 ** -13 * ref.S"),
+        COMPARE),
+    "bound without the output rounding": (
+        ("fp_bound", "    if out_fmt in _OUT_ROUNDING:", "    if False:"), COMPARE),
+    "NaN results not required": (
+        ("check_fp", "        bad |= nan_v & ~np.isnan(Dv)\n", "\n"), COMPARE),
+    "infinite results not required": (
+        ("check_fp", "        bad |= inf_v & ~(Dv == v)\n", "\n"), COMPARE),
+    "exact mode takes NaN as unequal": (
+        ("check_fp", "same = (Dv == ref_rounded) | (np.isnan(Dv) & np.isnan(ref_rounded))",
+         "same = (Dv == ref_rounded)"), COMPARE),
+    "INT32 check tolerates 1": (
+        ("check_int", "bad = d != r", "bad = np.abs(d.astype(np.int64) - r) > 1"), COMPARE),
+    "three-BF16: A pieces hi, lo, lo": (("bf16x3_operands", "(ah, al, ah)", "(ah, al, al)"), SPLIT),
+    "three-BF16: B pieces hi, lo, hi": (("bf16x3_operands", "(bh, bh, bl)", "(bh, bl, bh)"), SPLIT),
+    "three-BF16: pieces not padded to 8": (
+        ("bf16x3_operands", "    kp = _rup8(k)", "    kp = k"), SPLIT),
+    "FP8 bound without the truncation term": (
+        ("fp8_bound", "(FP8_TRUNCATION + keff * 2.0 ** -23)", "(keff * 2.0 ** -23)"),
+        FP8 + ["tests/test_oracle_fp8_model.py"]),
+}
+
+
+def _python_plant(spec):
+    fn, old, new = spec
+    return ("import inspect, oracle\n"
+            f"_s = inspect.getsource(oracle.{fn})\n"
+            f"assert _s.count({old!r}) == 1, 'the planted text must be unique'\n"
+            f"exec(compile(_s.replace({old!r}, {new!r}), oracle.__file__, 'exec'), oracle.__dict__)\n")
+
+
+def test_every_planted_python_mistake_fails_a_pin():
+    assert survivors({}, PYTHON, _python_plant) == []
+
+
 def _model_params(kw):
     return ("import functools, oracle\n"
             f"oracle.gemm_mfma = functools.partial(oracle.gemm_mfma, **{kw!r})\n")
@@ -142,4 +186,4 @@ def test_every_planted_mistake_fails_a_pin():
 
 
 def test_the_unmutated_oracle_passes_its_pins():
-    assert not pins_fail(GEMM + FORMATS + MODEL + SP24 + SPLIT + FP8)
+    assert not pins_fail(GEMM + FORMATS + MODEL + SP24 + SPLIT + FP8 + COMPARE)
