@@ -108,6 +108,10 @@ CODE = {
         "int oracle_gemm_sp24_mfma_points(", "(2 * (j % 4))", "(6 - 2 * (j % 4))", SP24),
     "sparse INT8: positions read from the high bits": (
         "int oracle_gemm_sp24_int_points(", "(2 * (j % 4))", "(6 - 2 * (j % 4))", SP24),
+    "sparse FP8: positions read from the high bits": (
+        "int oracle_gemm_sp24_fp8_points(", "(2 * (j % 4))", "(6 - 2 * (j % 4))", SP24),
+    "sparse FP8 model: positions read from the high bits": (
+        "int oracle_gemm_sp24_fp8_mfma_points(", "(2 * (j % 4))", "(6 - 2 * (j % 4))", SP24),
     "split: high piece cut instead of rounded": (
         "int oracle_split_bf16(", "const uint64_t h = oracle_encode_rne(v, 8, 7);",
         "const uint64_t h = (union { float f; uint32_t u; }){ (float)v }.u >> 16;", SPLIT),
