@@ -278,6 +278,12 @@ WORKLOADS = {
         note="FP16 ragged 5000x3000x1000, fp16 output rounded RNE from fp32"),
 }
 
+# The INT8 workload with beta = 1: C (zeros, 64 MiB of INT32) is read and added.
+WORKLOADS["i8_4096_nn_beta1"] = Workload(
+    "i8_4096_nn_beta1", "i8", "i32", 4096, 4096, 4096, alpha=1, beta=1,
+    a_dist="int_uniform(-128,127)", b_dist="int_uniform(-128,127)", c_dist="zeros", seed=3,
+    note="INT8 4096^3 row-major as above, alpha = beta = 1: C = 0 read and added")
+
 # The same ragged workload with genuinely padded leading dimensions.
 WORKLOADS["f16_5000x3000x1000_f16out_padded"] = Workload(
     "f16_5000x3000x1000_f16out_padded", "f16", "f16", 5000, 3000, 1000, alpha=1.0, beta=0.0,

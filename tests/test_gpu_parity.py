@@ -207,8 +207,8 @@ def test_workload_int8_4096_nn_full_and_in_place_beta1():
     rep, res = check_case(w)
     _assert(rep, res)
     # beta = 1 with C = 0 and D written over C in place: identical bits
-    w1 = Workload(w.name + "_beta1", w.in_type, w.out_type, w.m, w.n, w.k, alpha=1, beta=1,
-                  a_dist=w.a_dist, b_dist=w.b_dist, c_dist="zeros", seed=w.seed)
+    w1 = WORKLOADS["i8_4096_nn_beta1"]
+    assert (w1.a_dist, w1.b_dist, w1.seed, w1.c_dist) == (w.a_dist, w.b_dist, w.seed, "zeros")
     inp1 = generate(w1)
     res1 = run_gpu(inp1, in_place=True)
     assert np.array_equal(res1.D[:, : w.n], res.D[:, : w.n])
