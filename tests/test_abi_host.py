@@ -99,6 +99,7 @@ def test_sizes_and_nulls():
     assert chk(D=None) == ST["INVALID_VALUE"]
     assert chk(beta=1.0, C=None) == ST["INVALID_VALUE"]                # C needed when beta != 0
     assert chk(beta=0.0, C=None) == ST["SUCCESS"]                      # not read when beta == 0
+    assert chk(beta=-0.0, C=None) == ST["SUCCESS"]                     # -0 is zero: not read
     assert chk(beta=float("nan"), C=None) == ST["INVALID_VALUE"]       # NaN beta reads C
     lib = mp.load()
     one = ctypes.c_float(1.0)
@@ -145,6 +146,8 @@ def test_types_outside_the_matrix_are_not_supported():
 def test_alignment_contract():
     assert chk(A=P + 8) == ST["NOT_SUPPORTED"]
     assert chk(D=P + 4) == ST["NOT_SUPPORTED"]
+    assert chk(beta=1.0, C=P + 8) == ST["NOT_SUPPORTED"]                    # C read: aligned
+    assert chk(beta=0.0, C=P + 8) == ST["SUCCESS"]                          # C not read
     assert chk(k=60, lda=60, ldb=64) == ST["NOT_SUPPORTED"]                  # 120 B rows
     assert chk(n=60, ldb=60, ldc=64) == ST["NOT_SUPPORTED"]
     assert chk(ldc=66) == ST["NOT_SUPPORTED"]
@@ -275,6 +278,8 @@ def test_sp24_contract():
     assert chk_sp(compute_type="i32") == ST["NOT_SUPPORTED"]
     # k a multiple of 128; k = 0 allowed (D = beta C), with null operands
     assert chk_sp(k=200, lda=104, ld_meta=32, ldb=200) == ST["NOT_SUPPORTED"]
+    assert chk_sp(k=192, lda=96, ld_meta=32, ldb=192) == ST["NOT_SUPPORTED"]   # 64 | k, 128 does not
+    assert chk_sp(k=64, lda=32, ld_meta=16, ldb=64) == ST["NOT_SUPPORTED"]
     assert chk_sp(k=0, lda=8, ld_meta=16, ldb=8, Ac=None, meta=None, B=None) == ST["SUCCESS"]
     # leading-dimension minimums and alignment
     assert chk_sp(lda=120) == ST["INVALID_VALUE"]
