@@ -25,14 +25,15 @@ def plant(src: str, fn: str, old: str, new: str) -> str:
     return src[:pos] + new + src[pos + len(old):]
 
 
-def pins_fail(files, lib=None, prelude="") -> bool:
-    """True when at least one pin of `files` fails (and none errors) with the oracle library
-    `lib` (None: the built one) after `prelude` has run."""
+def pins_fail(files, lib=None, prelude="", lib_var="MPGEMM_ORACLE_LIB", args=()) -> bool:
+    """True when at least one pin of `files` fails (and none errors) with the library `lib`
+    (None: the built one) named by `lib_var`, after `prelude` has run."""
     env = dict(os.environ, OMP_NUM_THREADS="1")
     if lib is not None:
-        env["MPGEMM_ORACLE_LIB"] = lib
+        env[lib_var] = lib
     code = (prelude + "import sys, pytest\n"
-            f"sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider'] + {list(files)!r}))\n")
+            "sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider', '-m', 'not gpu'] + "
+            f"{list(files) + list(args)!r}))\n")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
                        text=True, timeout=600)
     return r.returncode == 1 and " failed" in r.stdout
@@ -63,4 +64,30 @@ def survivors(code: dict, params: dict, param_prelude) -> list:
 
         results = list(pool.map(one_code, enumerate(sorted(code.items()))))
         results += list(pool.map(one_param, sorted(params.items())))
+    return [name for name, caught in results if not caught]
+
+
+HOST_SRC = os.path.join(ROOT, "mixed_precision_dense_amd", "csrc", "mpgemm_host.cpp")
+
+
+def host_survivors(code: dict, files, args=()) -> list:
+    """Names of the mistakes in the library's host-only argument checks (mpgemm_host.cpp,
+    built alone with g++ and loaded through MPGEMM_HOST_CHECK_LIB) that no test of `files`
+    catches.  code: name -> (function, old, new)."""
+    src = open(HOST_SRC).read()
+    csrc = os.path.dirname(HOST_SRC)
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with tempfile.TemporaryDirectory() as tmp, ThreadPoolExecutor(workers) as pool:
+        def one(item):
+            t, (name, (fn, old, new)) = item
+            path = os.path.join(tmp, f"h{t}")
+            with open(path + ".cpp", "w") as f:
+                f.write(plant(src, fn, old, new))
+            subprocess.run(["g++", "-std=c++17", "-fPIC", "-shared", "-O1",
+                            "-I" + os.path.join(ROOT, "include"), "-I" + csrc, "-o",
+                            path + ".so", path + ".cpp"], check=True)
+            return name, pins_fail(files, lib=path + ".so", lib_var="MPGEMM_HOST_CHECK_LIB",
+                                   args=args)
+
+        results = list(pool.map(one, enumerate(sorted(code.items()))))
     return [name for name, caught in results if not caught]
